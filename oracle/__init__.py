@@ -1,0 +1,33 @@
+"""CPU oracle for the fixed-width LayerNorm / shifted-window gather row pipeline.
+
+TEST INFRASTRUCTURE. Only the tests, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` import this package. The product path (the
+HIP library under ``include/lwg.h`` and its Python binding) never imports,
+calls or links anything here, and this package imports nothing from it.
+
+Everything is plain numpy in float64, written from the definitions on the page
+"Pangu-Weather inference optimisation on Hygon BW1000 (gfx936)"
+(l189.com/news/2144533):
+
+* ``residual_sum`` -- section 4 (fused residual add + norm: the residual is
+  rounded to FP16 once, before the normalisation reads it);
+* ``layer_norm`` -- section 3 (fixed-width LayerNorm, no affine, widths 192/384);
+* ``window_token_count`` / ``window_index_table`` -- section 5 (INT32 index
+  table per window shape, padding folded into the index protocol);
+* ``window_gather`` -- section 5 (index >= 0 copies the source token, -1 writes
+  a zero row);
+* ``norm_gather`` -- section 5 (norm1's output feeds only the window gather).
+
+Each function is pinned by ``tests/test_oracle_pins.py`` to closed forms,
+brute force on tiny inputs, a library routine, or values derived by hand and
+stored under ``tests/golden/``.
+"""
+from .rowops import EPS, WIDTHS, fp16_round, residual_sum, layer_norm, add_ln
+from .window import (padded_extent, window_token_count, window_index_table,
+                     window_gather, norm_gather, norm_gather_rows)
+
+__all__ = [
+    "EPS", "WIDTHS", "fp16_round", "residual_sum", "layer_norm", "add_ln",
+    "padded_extent", "window_token_count", "window_index_table", "window_gather",
+    "norm_gather", "norm_gather_rows",
+]

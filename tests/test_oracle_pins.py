@@ -1,0 +1,322 @@
+"""Pins of the CPU oracle to things other than itself.
+
+Each test fixes one oracle function against what the pages and the mathematics
+determine: IEEE binary16 rounding done in exact rational arithmetic, closed
+forms of LayerNorm on special rows, a library LayerNorm, invariants, tables
+derived by hand (tests/golden/), and brute force on tiny grids. A plausible slip
+in the oracle (a dropped eps, an unbiased variance, a wrong roll sign, a swapped
+window order, padding at the wrong end) fails at least one of them.
+"""
+import json
+import os
+from decimal import Decimal, getcontext
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+# ---------------------------------------------------------------------------
+# helpers that are independent of the oracle's arithmetic
+
+
+def f16_from_bits(bits):
+    return np.array(bits, dtype=np.uint16).view(np.float16)
+
+
+def bits_of(a):
+    return np.asarray(a, dtype=np.float16).view(np.uint16)
+
+
+def rne_binary16_exact(q: Fraction):
+    """Round an exact rational to binary16, ties to even, by counting ulps.
+    Returns a Python float holding the rounded value (or +-inf)."""
+    if q == 0:
+        return 0.0
+    sign = -1.0 if q < 0 else 1.0
+    a = abs(q)
+    if a >= Fraction(65520):           # midpoint of 65504 and 2**16: ties go to 2**16 -> inf
+        return sign * float("inf")
+    if a < Fraction(1, 2 ** 14):
+        ulp = Fraction(1, 2 ** 24)     # subnormal spacing
+    else:
+        e = a.numerator.bit_length() - a.denominator.bit_length()
+        if Fraction(2) ** e > a:
+            e -= 1
+        ulp = Fraction(2) ** (e - 10)
+    m = a / ulp
+    n = m.numerator // m.denominator
+    r = m - n
+    if r > Fraction(1, 2) or (r == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return sign * float(n * ulp)
+
+
+# ---------------------------------------------------------------------------
+# residual_sum: FP16(residual + branch), rounded once
+
+
+def test_residual_golden_cases(golden_dir):
+    spec = json.load(open(os.path.join(golden_dir, "fp16_residual_cases.json")))
+    for case in spec["cases"]:
+        r = f16_from_bits([int(case["residual"], 16)])
+        b = f16_from_bits([int(case["branch"], 16)])
+        got = oracle.residual_sum(r, b)
+        if case["expect"] == "nan":
+            assert np.isnan(got[0]), case
+        else:
+            assert int(bits_of(got)[0]) == int(case["expect"], 16), case
+
+
+def _finite_f16_bits(rng, n):
+    bits = rng.integers(0, 1 << 16, size=4 * n, dtype=np.uint32).astype(np.uint16)
+    bits = bits[(bits & 0x7C00) != 0x7C00]
+    return bits[:n]
+
+
+def test_residual_matches_exact_rational_rounding():
+    rng = np.random.default_rng(11)
+    n = 6000
+    a = _finite_f16_bits(rng, n)
+    b = _finite_f16_bits(rng, n)
+    # near-cancellation and same-binade pairs, where rounding decisions are dense
+    c = _finite_f16_bits(rng, n)
+    d = (c.astype(np.int32) ^ 0x8000) + rng.integers(-40, 41, size=n)
+    d = np.clip(d, 0, 0xFFFF).astype(np.uint16)
+    d[(d & 0x7C00) == 0x7C00] = 0
+    ra = np.concatenate([a, c]).view(np.float16)
+    rb = np.concatenate([b, d]).view(np.float16)
+    got = bits_of(oracle.residual_sum(ra, rb))
+    for x, y, g in zip(ra.tolist(), rb.tolist(), got.tolist()):
+        exact = Fraction(x) + Fraction(y)
+        v = rne_binary16_exact(exact)
+        if exact == 0 and x == 0.0 and y == 0.0 and str(x)[0] == "-" and str(y)[0] == "-":
+            v = -0.0
+        assert g == int(np.float16(v).view(np.uint16)), (x, y, hex(g), v)
+
+
+def test_residual_rounds_once_not_in_fp32_normalisation():
+    # the LayerNorm reads the rounded residual: add_ln's y equals layer_norm of
+    # its own residual output, not of the unrounded sum
+    rng = np.random.default_rng(12)
+    br = workloads.normal_rows(3, 8, 192)
+    res = (rng.normal(size=(8, 192)) * 1e3).astype(np.float16)
+    r, y = oracle.add_ln(br, res)
+    assert np.array_equal(bits_of(r), bits_of(oracle.residual_sum(res, br)))
+    assert np.array_equal(bits_of(y), bits_of(oracle.layer_norm(r)))
+
+
+# ---------------------------------------------------------------------------
+# layer_norm
+
+
+@pytest.mark.parametrize("C", [192, 384])
+def test_ln_plus_minus_one_row(C):
+    row = np.array([1.0] * (C // 2) + [-1.0] * (C // 2), dtype=np.float16)[None, :]
+    y = oracle.layer_norm(row)
+    # mean 0, biased variance 1: y = +-1/sqrt(1 + 1e-5) = +-0.999995 -> +-1.0 in binary16
+    assert np.array_equal(bits_of(y)[0, : C // 2], np.full(C // 2, 0x3C00, np.uint16))
+    assert np.array_equal(bits_of(y)[0, C // 2:], np.full(C // 2, 0xBC00, np.uint16))
+
+
+@pytest.mark.parametrize("C", [192, 384])
+@pytest.mark.parametrize("value", [0.0, 3.5, -100.0, 65504.0])
+def test_ln_constant_row_is_plus_zero(C, value):
+    row = np.full((1, C), value, dtype=np.float16)
+    assert np.array_equal(bits_of(oracle.layer_norm(row)), np.zeros((1, C), np.uint16))
+
+
+def _two_valued_expected(C, k, a, b, eps=1e-5):
+    """Closed form for a row with k entries a and C-k entries b:
+    mean = (k a + (C-k) b)/C, biased var = k (C-k) (a-b)^2 / C^2,
+    y_a = (C-k)(a-b)/C / sqrt(var+eps), y_b = -k (a-b)/C / sqrt(var+eps)."""
+    getcontext().prec = 60
+    A, B, D = Decimal(a), Decimal(b), Decimal(a) - Decimal(b)
+    var = Decimal(k) * Decimal(C - k) * D * D / Decimal(C * C)
+    den = (var + Decimal(eps)).sqrt()
+    ya = Decimal(C - k) * D / Decimal(C) / den
+    yb = -Decimal(k) * D / Decimal(C) / den
+    return np.float16(float(ya)), np.float16(float(yb))
+
+
+@pytest.mark.parametrize("C", [192, 384])
+@pytest.mark.parametrize("k,a,b", [(1, 2.0, 0.0), (5, 1.5, -0.25), (96, 2.0 ** -10, -(2.0 ** -10)),
+                                   (37, 100.0, 101.0), (150, -3.0, 7.0), (3, 0.0078125, 0.0)])
+def test_ln_two_valued_rows_closed_form(C, k, a, b):
+    row = np.array([a] * k + [b] * (C - k), dtype=np.float16)[None, :]
+    ya, yb = _two_valued_expected(C, k, float(row[0, 0]), float(row[0, -1]))
+    y = oracle.layer_norm(row)
+    assert np.all(bits_of(y[0, :k]) == bits_of(ya)), (y[0, 0], ya)
+    assert np.all(bits_of(y[0, k:]) == bits_of(yb)), (y[0, -1], yb)
+
+
+@pytest.mark.parametrize("C", [192, 384])
+def test_ln_matches_torch_layer_norm_float64(C):
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(21 + C)
+    x = np.concatenate([
+        rng.normal(0, 1, size=(400, C)),
+        rng.normal(100, 1, size=(50, C)),
+        rng.normal(0.5, 2, size=(50, C)) * 50,
+        rng.normal(0, 1, size=(50, 1)) + 1e-3 * rng.normal(0, 1, size=(50, C)),
+    ]).astype(np.float16)
+    ref = torch.nn.functional.layer_norm(torch.from_numpy(x.astype(np.float64)), (C,), eps=1e-5)
+    ref16 = ref.numpy().astype(np.float16)
+    assert np.array_equal(bits_of(oracle.layer_norm(x)), bits_of(ref16))
+
+
+@pytest.mark.parametrize("C", [192, 384])
+def test_ln_row_invariants(C):
+    rng = np.random.default_rng(31 + C)
+    x = np.concatenate([
+        rng.normal(0, 1, size=(200, C)),
+        rng.normal(100, 1, size=(50, C)),
+        rng.normal(0, 1, size=(50, 1)) + 1e-3 * rng.normal(0, 1, size=(50, C)),
+    ]).astype(np.float16)
+    y = oracle.layer_norm(x).astype(np.float64)
+    v = x.astype(np.float64).var(axis=1)
+    assert np.max(np.abs(y.mean(axis=1))) <= 1e-3
+    assert np.max(np.abs(y.var(axis=1) - v / (v + 1e-5))) <= 1e-3
+
+
+def test_ln_power_of_two_scale_and_shift_invariance():
+    # LN(4x + 8) vs LN(x): both transformations are exact in binary16 for these
+    # magnitudes; only eps breaks the invariance, by ~eps/var
+    x = workloads.normal_rows(41, 64, 192).astype(np.float64)
+    x = (np.clip(np.round(x * 64) / 64, -3.9, 3.9)).astype(np.float16)   # multiples of 2**-6
+    x2 = (x.astype(np.float64) * 4 + 8).astype(np.float16)
+    assert np.array_equal(x2.astype(np.float64), x.astype(np.float64) * 4 + 8)
+    d = np.abs(oracle.layer_norm(x2).astype(np.float64) - oracle.layer_norm(x).astype(np.float64))
+    assert d.max() <= 2e-3
+
+
+def test_ln_nonfinite_rows_become_nan_rows():
+    x = workloads.normal_rows(42, 4, 192)
+    x[1, 7] = np.inf
+    x[2, 0] = np.nan
+    y = oracle.layer_norm(x)
+    assert np.isnan(y[1]).all() and np.isnan(y[2]).all()
+    assert np.isfinite(y[0]).all() and np.isfinite(y[3]).all()
+
+
+def test_ln_rejects_other_widths():
+    with pytest.raises(ValueError):
+        oracle.layer_norm(np.zeros((2, 256), np.float16))
+
+
+# ---------------------------------------------------------------------------
+# window tables
+
+
+def brute_force_table(grid, window, shift):
+    """Loop form: visit windows and their tokens in order, map each gathered
+    position to the padded grid, apply the cyclic shift and test the real grid."""
+    Z, H, W = grid
+    wz, wh, ww = window
+    Zp, Hp, Wp = (-(-Z // wz) * wz, -(-H // wh) * wh, -(-W // ww) * ww)
+    out = []
+    for bz in range(Zp // wz):
+        for bh in range(Hp // wh):
+            for bw in range(Wp // ww):
+                for dz in range(wz):
+                    for dh in range(wh):
+                        for dw in range(ww):
+                            qz = (bz * wz + dz + shift[0]) % Zp
+                            qh = (bh * wh + dh + shift[1]) % Hp
+                            qw = (bw * ww + dw + shift[2]) % Wp
+                            if qz < Z and qh < H and qw < W:
+                                out.append((qz * H + qh) * W + qw)
+                            else:
+                                out.append(-1)
+    return np.array(out, dtype=np.int32)
+
+
+def test_window_table_golden_points(golden_dir):
+    spec = json.load(open(os.path.join(golden_dir, "window_table_points.json")))
+    for case in spec["cases"]:
+        grid, window, shift = tuple(case["grid"]), tuple(case["window"]), tuple(case["shift"])
+        t = oracle.window_index_table(grid, window, shift)
+        assert t.dtype == np.int32
+        assert oracle.window_token_count(grid, window) == case["rows"] == t.shape[0]
+        assert int((t == -1).sum()) == case["pads"]
+        for j, v in case["points"].items():
+            assert int(t[int(j)]) == v, (case["grid"], case["shift"], j)
+        if "first_pad" in case:
+            assert int(np.argmax(t == -1)) == case["first_pad"]
+
+
+@pytest.mark.parametrize("grid", [(2, 12, 24), (2, 7, 13), (4, 9, 26), (3, 6, 12), (1, 1, 1), (5, 11, 25)])
+@pytest.mark.parametrize("shift", [(0, 0, 0), (1, 3, 6), (0, 5, 11), (3, 13, 30)])
+def test_window_table_matches_brute_force(grid, shift):
+    window = workloads.WINDOW
+    t = oracle.window_index_table(grid, window, shift)
+    assert np.array_equal(t, brute_force_table(grid, window, shift))
+
+
+@pytest.mark.parametrize("level", [workloads.LEVEL1, workloads.LEVEL2])
+@pytest.mark.parametrize("shift", [workloads.NO_SHIFT, workloads.SHIFT])
+def test_window_table_is_a_bijection_onto_tokens(level, shift):
+    t = oracle.window_index_table(level.grid, workloads.WINDOW, shift)
+    valid = np.sort(t[t >= 0])
+    assert np.array_equal(valid, np.arange(level.tokens, dtype=np.int32))
+    assert int((t == -1).sum()) == t.shape[0] - level.tokens
+    assert int(t.min()) >= -1
+
+
+def test_window_table_special_cases():
+    # one window covering the whole grid, no shift: identity
+    assert np.array_equal(oracle.window_index_table((2, 6, 12), (2, 6, 12)), np.arange(144))
+    # unit windows, no shift: identity in grid order
+    assert np.array_equal(oracle.window_index_table((3, 5, 7), (1, 1, 1)), np.arange(105))
+    # a shift by a whole padded extent is no shift
+    a = oracle.window_index_table((8, 20, 30), (2, 6, 12), (0, 0, 0))
+    b = oracle.window_index_table((8, 20, 30), (2, 6, 12), (8, 24, 36))
+    assert np.array_equal(a, b)
+    # unit windows with a shift: a plain cyclic roll of the token ids
+    t = oracle.window_index_table((1, 1, 10), (1, 1, 1), (0, 0, 3))
+    assert t.tolist() == [3, 4, 5, 6, 7, 8, 9, 0, 1, 2]
+
+
+# ---------------------------------------------------------------------------
+# gathers
+
+
+def test_window_gather_brute_force_with_pads_and_bad_entries():
+    rng = np.random.default_rng(51)
+    x = workloads.normal_rows(52, 50, 192)
+    table = rng.integers(-1, 50, size=300).astype(np.int32)
+    table[::17] = 50          # one past the end: a zero row, not a read
+    table[5] = -7             # any other negative entry: a zero row
+    out = oracle.window_gather(x, table)
+    for j, t in enumerate(table.tolist()):
+        if 0 <= t < 50:
+            assert np.array_equal(bits_of(out[j]), bits_of(x[t]))
+        else:
+            assert not bits_of(out[j]).any()   # +0.0 bits
+
+
+def test_window_gather_id_encoded_rows_decode_to_the_table():
+    # each source row carries its own index as exact binary16 integers
+    grid = (8, 20, 30)
+    n = 8 * 20 * 30
+    x = np.zeros((n, 192), np.float16)
+    ids = np.arange(n)
+    x[:, 0] = ids % 2048
+    x[:, 1] = ids // 2048
+    x[:, 2] = 1.0
+    t = oracle.window_index_table(grid, workloads.WINDOW, workloads.SHIFT)
+    g = oracle.window_gather(x, t).astype(np.int64)
+    decoded = np.where(g[:, 2] == 1, g[:, 0] + 2048 * g[:, 1], -1)
+    assert np.array_equal(decoded, t.astype(np.int64))
+
+
+def test_norm_gather_rows_agrees_with_full_norm_gather():
+    x = workloads.normal_rows(61, 576, 192)
+    x[3] = np.float16(2.5)  # a constant row
+    t = oracle.window_index_table((2, 12, 24), workloads.WINDOW, workloads.SHIFT)
+    full = oracle.norm_gather(x, t)
+    rows = np.array([0, 1, 100, 575, int(np.argmax(t == 3))])
+    assert np.array_equal(bits_of(oracle.norm_gather_rows(x, t, rows)), bits_of(full[rows]))
+    assert not bits_of(full[int(np.argmax(t == 3))]).any()
