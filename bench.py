@@ -1,0 +1,336 @@
+"""Throughput of the row pipeline on one MI355X, in achieved HBM GB/s.
+
+One step is one pass of the whole hot path at both model widths: for level 1
+([131040, 192], grid 8x182x90) and level 2 ([32760, 384], grid 8x91x45):
+ln_fixed, add_ln, window_index_build (window (2,6,12), shift (1,3,6)),
+window_gather and the fused norm_gather. Inputs are seeded synthetic tensors
+(workloads.py) already resident in HBM. Every op of a step reads its own copy
+of the inputs, and R sets of buffers rotate across steps, so no timed launch
+finds its data in the 256 MB Infinity Cache from an earlier launch.
+
+Output: one JSON line (see the keys below). ``value`` is algorithmic bytes of a
+step / wall time of a step. ``roofline`` is the dominant kernel (add_ln at
+level 1), timed with HIP events around each of its launches inside the timed
+steps. ``kernels`` times every op alone, with HIP events around each launch.
+``cpu_baseline`` times the CPU oracle on one full step of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+from workloads import LEVEL1, LEVEL2, WINDOW, SHIFT  # noqa: E402
+
+METRIC = "achieved HBM GB/s (% of peak) + Mtokens/s, fused add_ln/norm_gather C=192/384"
+PEAK_GBS = 8000.0          # MI355X HBM3E, AMD's published peak
+HALF = 2                   # bytes per binary16
+INDEX = 4                  # bytes per int32 table entry
+PMC_FILE = os.path.join(ROOT, "profiles", "add_ln_level1_pmc.json")
+KERNEL_SOURCE = os.path.join(ROOT, "layernorm_window_gather_amd", "csrc", "lwg_kernels.hip")
+
+
+def algorithmic_bytes(op: str, n: int, m: int, c: int) -> int:
+    """Bytes the operation itself must move (fp16 = 2 B, index = 4 B). Gathers
+    read each source row once (the table is a bijection onto the tokens plus
+    padding rows, which read nothing), write every output row, read the table."""
+    if op == "ln_fixed":
+        return 2 * n * c * HALF
+    if op == "add_ln":
+        return 4 * n * c * HALF
+    if op == "window_index_build":
+        return INDEX * m
+    if op in ("window_gather", "norm_gather"):
+        return n * c * HALF + m * c * HALF + INDEX * m
+    raise ValueError(op)
+
+
+OPS = ("ln_fixed", "add_ln", "window_index_build", "window_gather", "norm_gather")
+
+
+def level_inputs(level):
+    if level is LEVEL1:
+        x, residual = workloads.level1_inputs()
+    else:
+        x, residual, _ = workloads.level2_inputs()
+    return x, residual
+
+
+class LevelBuffers:
+    """One rotation set of device buffers for one level."""
+
+    def __init__(self, lwg, torch, dev, level, x_dev, res_dev, m):
+        n, c = level.tokens, level.channels
+        e = lambda rows: torch.empty(rows, c, dtype=torch.float16, device=dev)  # noqa: E731
+        self.x = {op: x_dev.clone() for op in ("ln_fixed", "add_ln", "window_gather", "norm_gather")}
+        self.res = res_dev.clone()
+        self.y_ln, self.r_out, self.y_add = e(n), e(n), e(n)
+        self.g_out, self.ng_out = e(m), e(m)
+        self.table = torch.empty(m, dtype=torch.int32, device=dev)
+        self.calls = {
+            "ln_fixed": lwg.prepare("ln_fixed", self.x["ln_fixed"], self.y_ln),
+            "add_ln": lwg.prepare("add_ln", self.x["add_ln"], self.res, self.r_out, self.y_add),
+            "window_index_build": lwg.prepare("window_index_build", self.table, grid=level.grid,
+                                              window=WINDOW, shift=SHIFT),
+            "window_gather": lwg.prepare("window_gather", self.x["window_gather"], self.table, self.g_out),
+            "norm_gather": lwg.prepare("norm_gather", self.x["norm_gather"], self.table, self.ng_out),
+        }
+
+
+def parity_gate(lwg, torch, sets, host, levels, m_of):
+    """Sampled parity of every op on the bench buffers before any timing."""
+    import oracle
+    rng = np.random.default_rng(123)
+    for lv in levels:
+        b = sets[0][lv.name]
+        for op in OPS:
+            b.calls[op]()
+        torch.cuda.synchronize()
+        x, residual = host[lv.name]
+        table = oracle.window_index_table(lv.grid, WINDOW, SHIFT)
+        if not np.array_equal(b.table.cpu().numpy(), table):
+            raise SystemExit(f"parity gate: window table differs at {lv.name}")
+        rows = np.unique(np.concatenate([rng.choice(lv.tokens, 1024, replace=False), [0, lv.tokens - 1]]))
+        jrows = np.unique(np.concatenate([rng.choice(m_of[lv.name], 1024, replace=False), [m_of[lv.name] - 1]]))
+        r_ref, y_ref = oracle.add_ln(x[rows], residual[rows])
+        checks = [
+            ("ln_fixed", b.y_ln.cpu().numpy()[rows], oracle.layer_norm(x[rows]), False),
+            ("add_ln residual", b.r_out.cpu().numpy()[rows], r_ref, True),
+            ("add_ln", b.y_add.cpu().numpy()[rows], y_ref, False),
+            ("window_gather", b.g_out.cpu().numpy()[jrows], oracle.window_gather(x, table[jrows]), True),
+            ("norm_gather", b.ng_out.cpu().numpy()[jrows], oracle.norm_gather_rows(x, table, jrows), False),
+        ]
+        for name, got, ref, exact in checks:
+            if exact:
+                ok = np.array_equal(got.view(np.uint16), ref.view(np.uint16))
+            else:
+                d = np.abs(got.astype(np.float64) - ref.astype(np.float64))
+                ok = d.max() <= 2e-3 and d.mean() <= 1e-4
+            if not ok:
+                raise SystemExit(f"parity gate failed: {name} at {lv.name}")
+    return True
+
+
+def kernel_source_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_profile(dominant_bytes):
+    """HBM bytes per launch of the dominant kernel from committed rocprofv3 PMC
+    counters (FETCH_SIZE + WRITE_SIZE, scaled by a copy-kernel calibration), or
+    None when absent or taken on a different kernel source."""
+    try:
+        rec = json.load(open(PMC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(step_bytes, host, levels, min_seconds):
+    """The oracle (float64 numpy, single-threaded ufuncs) over full steps of the
+    same workload, repeated until at least ``min_seconds`` have passed (at most
+    30 steps); reported in GB/s of algorithmic bytes."""
+    import oracle
+    t0 = time.perf_counter()
+    repeats = 0
+    while repeats < 30 and (repeats == 0 or time.perf_counter() - t0 < min_seconds):
+        repeats += 1
+        for lv in levels:
+            x, residual = host[lv.name]
+            oracle.layer_norm(x)
+            oracle.add_ln(x, residual)
+            table = oracle.window_index_table(lv.grid, WINDOW, SHIFT)
+            oracle.window_gather(x, table)
+            oracle.norm_gather(x, table)
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(step_bytes * repeats / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{repeats} full step(s) of the same workload (both levels, all five ops) "
+                  f"in {dt:.1f} s; numpy ufuncs run on one thread; host has {os.cpu_count()} logical CPUs",
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--sets", type=int, default=3, help="rotating buffer sets")
+    ap.add_argument("--kernel-reps", type=int, default=100, help="launches per op in the per-kernel table")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="minimum oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=OPS, default=None,
+                    help="launch only this op, --steps times per level (for profiling runs)")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="also run an elementwise copy of this many MiB (PMC calibration)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported "
+              "(the row pipeline is sharded by rows/windows across GPUs; only the one-GPU shard is built)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import layernorm_window_gather_amd as lwg
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda", 0)
+    lwg.library()
+    props = torch.cuda.get_device_properties(dev)
+    levels = (LEVEL1, LEVEL2)
+    m_of = {lv.name: lwg.window_token_count(lv.grid, WINDOW) for lv in levels}
+
+    host = {lv.name: level_inputs(lv) for lv in levels}
+    sets = []
+    for s in range(args.sets):
+        per = {}
+        for lv in levels:
+            x, residual = host[lv.name]
+            xd = torch.from_numpy(x).to(dev)
+            rd = torch.from_numpy(residual).to(dev)
+            per[lv.name] = LevelBuffers(lwg, torch, dev, lv, xd, rd, m_of[lv.name])
+            del xd, rd
+        sets.append(per)
+    torch.cuda.synchronize()
+
+    parity_gate(lwg, torch, sets, host, levels, m_of)
+
+    bytes_of = {(lv.name, op): algorithmic_bytes(op, lv.tokens, m_of[lv.name], lv.channels)
+                for lv in levels for op in OPS}
+    step_bytes = sum(bytes_of.values())
+    stream = torch.cuda.current_stream(dev)
+
+    if args.only:
+        for lv in levels:
+            for i in range(args.warmup + args.steps):
+                sets[i % args.sets][lv.name].calls[args.only]()
+        torch.cuda.synchronize()
+        if args.calibration_copy_mib:
+            n = args.calibration_copy_mib * (1 << 20) // 2
+            a = torch.ones(n, dtype=torch.float16, device=dev)
+            b = torch.empty_like(a)
+            for _ in range(3):
+                torch.mul(a, 1, out=b)
+            torch.cuda.synchronize()
+        print(json.dumps({"profiling_run": args.only, "launches_per_level": args.warmup + args.steps}))
+        return 0
+
+    def step(i, ev=None):
+        per = sets[i % args.sets]
+        for lv in levels:
+            calls = per[lv.name].calls
+            calls["ln_fixed"]()
+            if ev is not None and lv is LEVEL1:
+                ev[0].record(stream)
+                calls["add_ln"]()
+                ev[1].record(stream)
+            else:
+                calls["add_ln"]()
+            calls["window_index_build"]()
+            calls["window_gather"]()
+            calls["norm_gather"]()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    dom_us = float(np.mean([a.elapsed_time(b) for a, b in events])) * 1e3
+    dom_bytes = bytes_of[(LEVEL1.name, "add_ln")]
+
+    # per-kernel table: each op alone, HIP events around every launch
+    kernels = {}
+    for lv in levels:
+        for op in OPS:
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.kernel_reps)]
+            for i in range(5):
+                sets[i % args.sets][lv.name].calls[op]()
+            torch.cuda.synchronize()
+            for i, (a, b) in enumerate(evs):
+                a.record(stream)
+                sets[i % args.sets][lv.name].calls[op]()
+                b.record(stream)
+            torch.cuda.synchronize()
+            us = np.array([a.elapsed_time(b) for a, b in evs]) * 1e3
+            med = float(np.median(us))
+            gbs = bytes_of[(lv.name, op)] / (med * 1e-6) / 1e9
+            kernels[f"{op}@{lv.name}"] = {
+                "C": lv.channels, "rows_in": lv.tokens,
+                "rows_out": m_of[lv.name] if op in ("window_gather", "norm_gather", "window_index_build") else lv.tokens,
+                "bytes": bytes_of[(lv.name, op)], "median_us": round(med, 2),
+                "p10_us": round(float(np.percentile(us, 10)), 2), "p90_us": round(float(np.percentile(us, 90)), 2),
+                "GBps": round(gbs, 1), "pct_of_peak": round(100 * gbs / PEAK_GBS, 1),
+                "Mtokens_per_s": round(lv.tokens / (med * 1e-6) / 1e6, 1),
+            }
+
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64",
+        "data": "synthetic",
+        "config": {
+            "workload": "row pipeline at both widths per step: ln_fixed, add_ln, window_index_build, "
+                        "window_gather, norm_gather on [131040,192] (grid 8x182x90) and [32760,384] "
+                        "(grid 8x91x45), window (2,6,12), shift (1,3,6)",
+            "io_dtype": "fp16", "statistics": "f64",
+            "step_bytes": step_bytes, "pct_of_peak": round(100 * value / PEAK_GBS, 1),
+            "buffer_sets": args.sets, "device": props.name,
+            "arch": getattr(props, "gcnArchName", "?"), "cus": props.multi_processor_count,
+        },
+        "roofline": {
+            "kernel": "add_ln@level1",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_GBS, 4),
+            "traffic": traffic_from_profile(dom_bytes),
+            "avg_launch_us": round(dom_us, 3),
+            "bytes_per_launch": dom_bytes,
+        },
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(step_bytes, host, levels, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,142 @@
+/*
+ * lwg.h -- C ABI of the fixed-width LayerNorm / shifted-window gather library
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operations are the memory-bound row pipeline of a Pangu-Weather-style 3D
+ * shifted-window transformer, as described on the page "Pangu-Weather inference
+ * optimisation on Hygon BW1000 (gfx936)" (l189.com/news/2144533), sections 3-5.
+ * The calling conventions (validate before launching, no launch on empty
+ * input, enqueue on the caller's stream, report launch errors) follow the page
+ * "PyTorch + HIP custom fused operator" (Hygon DCU practice series), section 6.
+ *
+ * Conventions shared by every call:
+ *  - Tensors are contiguous row-major [rows, C] arrays of IEEE 754 binary16.
+ *    Token rows of a (Z,H,W) grid are stored in (z,h,w) order, z slowest.
+ *  - Every tensor pointer is a device pointer, 16-byte aligned, allocated and
+ *    freed by the caller. The library never allocates, frees, synchronises or
+ *    changes the current device.
+ *  - `stream` is a hipStream_t passed as void*; NULL means the legacy default
+ *    stream. Work is enqueued asynchronously; a call returns before it runs.
+ *  - Arguments are checked on the host before any HIP call. A non-OK status
+ *    means nothing was enqueued; lwg_last_error() then describes the problem.
+ *  - rows == 0 (or n_out == 0) returns LWG_OK without launching anything; the
+ *    pointers are not inspected in that case.
+ *  - Only C = 192 and C = 384 are served (section 3 of the BW1000 page: the
+ *    model's widths are 192 and 384; other widths are refused, not served by an
+ *    untested path). Other widths return LWG_ERR_UNSUPPORTED_WIDTH.
+ *  - Statistics (row mean and biased variance) are accumulated in binary64 from
+ *    the binary16 inputs and each output is rounded once to binary16, to
+ *    nearest-even. LayerNorm has no scale or shift: the BW1000 page folds the
+ *    affine parameters into the following Linear at load time.
+ *  - Faults inside a kernel surface at the caller's next synchronisation.
+ */
+#ifndef LWG_H
+#define LWG_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LWG_ABI_VERSION 1
+
+typedef enum lwg_status {
+    LWG_OK = 0,
+    LWG_ERR_INVALID_ARGUMENT = 1,  /* null pointer, negative size, bad eps, bad window */
+    LWG_ERR_UNSUPPORTED_WIDTH = 2, /* C not in {192, 384} */
+    LWG_ERR_MISALIGNED = 3,        /* a tensor pointer not 16-byte aligned */
+    LWG_ERR_ALIASING = 4,          /* an output overlaps an input in a way the call forbids */
+    LWG_ERR_SIZE_MISMATCH = 5,     /* table length differs from the window token count */
+    LWG_ERR_HIP = 6                /* the HIP runtime reported an error at launch */
+} lwg_status;
+
+/*
+ * Fixed-width LayerNorm (BW1000 page, section 3).
+ *   y[r, :] = (x[r, :] - mean_r) / sqrt(var_r + eps), var_r biased (divide by C).
+ * x, y : [rows, C] binary16. y may equal x (in place); any other overlap is
+ *        LWG_ERR_ALIASING.
+ * eps  : finite and > 0 (1e-5 in the model).
+ * A row holding Inf or NaN yields a NaN row; a constant row yields +0.0.
+ */
+int32_t lwg_ln_fixed(const void* x, void* y, int64_t rows, int32_t C, double eps,
+                     void* stream);
+
+/*
+ * Residual add + LayerNorm (BW1000 page, section 4).
+ *   residual_out = FP16(residual + branch)      (exact sum rounded once, nearest-even)
+ *   y            = LayerNorm(residual_out)      (reads the rounded residual)
+ * All four tensors are [rows, C] binary16. residual_out may equal residual or
+ * branch (in-place update of the residual stream); y may equal residual or
+ * branch. y and residual_out must not overlap each other, and no output may
+ * partially overlap anything (LWG_ERR_ALIASING).
+ */
+int32_t lwg_add_ln(const void* branch, const void* residual, void* residual_out, void* y,
+                   int64_t rows, int32_t C, double eps, void* stream);
+
+/*
+ * Number of rows of the gathered tensor for a (Z,H,W) grid cut into
+ * (wz,wh,ww) windows: each extent is padded at its high end to a multiple of
+ * the window extent and the padded extents are multiplied. Host only (no HIP
+ * call). Returns -1 for a negative grid extent, a window extent < 1, or a
+ * count above INT32_MAX.
+ */
+int64_t lwg_window_token_count(int32_t Z, int32_t H, int32_t W,
+                               int32_t wz, int32_t wh, int32_t ww);
+
+/*
+ * INT32 shifted-window index table (BW1000 page, section 5: one INT32 index per
+ * gathered token, padding folded into the index protocol).
+ * Entry j (window-major: windows row-major over their (z,h,w) coordinates,
+ * tokens row-major inside a window) is the source token index of gathered row j,
+ * or -1 where that row is padding. The padded grid is rolled so that gathered
+ * position p reads padded position (p + shift) mod padded_extent on each axis.
+ * Shifts must be >= 0 and are taken modulo the padded extent.
+ * table     : device int32 [table_len], written by one kernel on `stream`.
+ * table_len : must equal lwg_window_token_count(Z,H,W,wz,wh,ww), else
+ *             LWG_ERR_SIZE_MISMATCH. The grid must hold at most INT32_MAX tokens.
+ */
+int32_t lwg_window_index_build(int32_t Z, int32_t H, int32_t W,
+                               int32_t wz, int32_t wh, int32_t ww,
+                               int32_t sz, int32_t sh, int32_t sw,
+                               int32_t* table, int64_t table_len, void* stream);
+
+/*
+ * Window token gather (BW1000 page, section 5).
+ *   out[j, :] = x[table[j], :]   if 0 <= table[j] < n_src
+ *             = +0.0             otherwise (-1 marks padding; any other
+ *                                out-of-range entry is treated the same way and
+ *                                never read)
+ * x     : [n_src, C] binary16 (may be NULL when n_src == 0).
+ * table : device int32 [n_out], 4-byte aligned.
+ * out   : [n_out, C] binary16; must not overlap x or table.
+ * n_src and n_out must not exceed INT32_MAX.
+ */
+int32_t lwg_window_gather(const void* x, int64_t n_src, int32_t C, const int32_t* table,
+                          int64_t n_out, void* out, void* stream);
+
+/*
+ * Fused norm-gather (BW1000 page, section 5: norm1's output is consumed only by
+ * the window gather, so the normalised tensor is never written).
+ *   out[j, :] = LayerNorm(x[table[j], :])  if 0 <= table[j] < n_src, else +0.0
+ * Same argument rules as lwg_window_gather, eps as in lwg_ln_fixed. Bitwise
+ * equal to lwg_ln_fixed followed by lwg_window_gather.
+ */
+int32_t lwg_norm_gather(const void* x, int64_t n_src, int32_t C, const int32_t* table,
+                        int64_t n_out, double eps, void* out, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* lwg_status_string(int32_t status);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if none).
+ * The pointer stays valid until the next lwg_* call on that thread. */
+const char* lwg_last_error(void);
+
+/* LWG_ABI_VERSION of the loaded library. */
+int32_t lwg_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LWG_H */

@@ -1,0 +1,262 @@
+"""MI355X (gfx950) row pipeline of a Pangu-Weather-style shifted-window transformer.
+
+Thin PyTorch binding over liblwg.so (include/lwg.h). PyTorch provides device
+memory and the current stream; every computation runs in the library's HIP
+kernels. Each function checks its tensors, allocates outputs that were not
+given, and calls the matching ``lwg_*`` entry point on
+``torch.cuda.current_stream(device)``. There is no CPU path: CPU tensors are
+refused.
+
+Operations (page "Pangu-Weather inference optimisation on Hygon BW1000
+(gfx936)", sections 3-5):
+  ln_fixed(x)                        LayerNorm of rows of width 192/384, no affine
+  add_ln(branch, residual)           (FP16(residual + branch), LayerNorm of it)
+  window_token_count(grid, window)   rows of the padded, windowed tensor
+  window_index_build(grid, window, shift)   INT32 table built on the device
+  window_table(grid, window, shift)  the same, cached per key and device
+  window_gather(x, table)            out[j] = x[table[j]], or zeros for -1
+  norm_gather(x, table)              out[j] = LayerNorm(x[table[j]]), or zeros
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import LwgError
+
+__all__ = ["ln_fixed", "add_ln", "window_token_count", "window_index_build", "window_table",
+           "window_gather", "norm_gather", "LwgError", "WIDTHS", "EPS", "library"]
+
+WIDTHS = (192, 384)
+EPS = 1e-5
+
+
+def library():
+    """The loaded ctypes handle of liblwg.so (raises if it is not built)."""
+    return _lib.load()
+
+
+def _stream(device: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t: torch.Tensor) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _rows(t: torch.Tensor, name: str) -> int:
+    """Check a [..., C] binary16 device tensor; return its row count."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != torch.float16:
+        raise RuntimeError(f"{name} must be float16, got {t.dtype}")
+    if t.dim() < 1 or t.shape[-1] not in WIDTHS:
+        raise RuntimeError(f"{name} must have last dimension 192 or 384, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise RuntimeError(f"{name} must be contiguous")
+    if t.device.type != "cuda":
+        raise RuntimeError(f"{name} must be on a GPU device, got {t.device}")
+    return t.numel() // t.shape[-1]
+
+
+def _same_device(ref: torch.Tensor, *others):
+    for name, t in others:
+        if t.device != ref.device:
+            raise RuntimeError(f"{name} is on {t.device}, expected {ref.device}")
+
+
+def _out_like(out, shape, device, name):
+    if out is None:
+        return torch.empty(shape, dtype=torch.float16, device=device)
+    _rows(out, name)
+    if tuple(out.shape) != tuple(shape):
+        raise RuntimeError(f"{name} has shape {tuple(out.shape)}, expected {tuple(shape)}")
+    if out.device != device:
+        raise RuntimeError(f"{name} is on {out.device}, expected {device}")
+    return out
+
+
+def ln_fixed(x: torch.Tensor, eps: float = EPS, out: torch.Tensor = None) -> torch.Tensor:
+    """LayerNorm over the last dimension (192 or 384) without affine; ``out`` may be ``x``."""
+    rows = _rows(x, "x")
+    y = _out_like(out, x.shape, x.device, "out")
+    lib = _lib.load()
+    with torch.cuda.device(x.device):
+        _lib.check(lib.lwg_ln_fixed(_ptr(x), _ptr(y), rows, x.shape[-1], float(eps), _stream(x.device)))
+    return y
+
+
+def add_ln(branch: torch.Tensor, residual: torch.Tensor, eps: float = EPS,
+           residual_out: torch.Tensor = None, out: torch.Tensor = None):
+    """Returns (FP16(residual + branch), LayerNorm of it). ``residual_out`` may be
+    ``residual`` or ``branch`` (in-place update); ``out`` may be either input."""
+    rows = _rows(residual, "residual")
+    _rows(branch, "branch")
+    if tuple(branch.shape) != tuple(residual.shape):
+        raise RuntimeError(f"branch shape {tuple(branch.shape)} != residual shape {tuple(residual.shape)}")
+    _same_device(residual, ("branch", branch))
+    r = _out_like(residual_out, residual.shape, residual.device, "residual_out")
+    y = _out_like(out, residual.shape, residual.device, "out")
+    lib = _lib.load()
+    with torch.cuda.device(residual.device):
+        _lib.check(lib.lwg_add_ln(_ptr(branch), _ptr(residual), _ptr(r), _ptr(y), rows,
+                                  residual.shape[-1], float(eps), _stream(residual.device)))
+    return r, y
+
+
+def _triple(v, name):
+    v = tuple(int(a) for a in v)
+    if len(v) != 3:
+        raise ValueError(f"{name} must have three entries (z, h, w)")
+    return v
+
+
+def window_token_count(grid, window) -> int:
+    """Rows of the gathered tensor: product of the extents padded up to the window."""
+    g, w = _triple(grid, "grid"), _triple(window, "window")
+    n = _lib.load().lwg_window_token_count(*g, *w)
+    if n < 0:
+        raise RuntimeError(f"invalid grid {g} / window {w}")
+    return int(n)
+
+
+def window_index_build(grid, window, shift=(0, 0, 0), device=None, out: torch.Tensor = None) -> torch.Tensor:
+    """Build the INT32 shifted-window index table on the device (one kernel)."""
+    g, w, s = _triple(grid, "grid"), _triple(window, "window"), _triple(shift, "shift")
+    m = window_token_count(g, w)
+    if out is None:
+        dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+        if dev.type != "cuda":
+            raise RuntimeError(f"window tables live on a GPU device, got {dev}")
+        out = torch.empty(m, dtype=torch.int32, device=dev)
+    elif out.dtype != torch.int32 or out.device.type != "cuda" or not out.is_contiguous() or out.dim() != 1:
+        raise RuntimeError("out must be a contiguous 1-D int32 GPU tensor")
+    lib = _lib.load()
+    with torch.cuda.device(out.device):
+        _lib.check(lib.lwg_window_index_build(*g, *w, *s, ctypes.c_void_p(out.data_ptr()), out.numel(),
+                                              _stream(out.device)))
+    return out
+
+
+_tables = {}
+
+
+def window_table(grid, window, shift=(0, 0, 0), device=None) -> torch.Tensor:
+    """Cached ``window_index_build``: one table per (grid, window, shift, device).
+    The table is built on the device's current stream at first use."""
+    g, w, s = _triple(grid, "grid"), _triple(window, "window"), _triple(shift, "shift")
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    if dev.index is None:
+        dev = torch.device("cuda", torch.cuda.current_device())
+    key = (g, w, s, dev.index)
+    t = _tables.get(key)
+    if t is None:
+        t = window_index_build(g, w, s, device=dev)
+        _tables[key] = t
+    return t
+
+
+def _gather_args(x, table, name):
+    n_src = _rows(x, "x")
+    if not isinstance(table, torch.Tensor) or table.dtype != torch.int32 or table.dim() != 1:
+        raise RuntimeError("table must be a 1-D int32 tensor")
+    if not table.is_contiguous():
+        raise RuntimeError("table must be contiguous")
+    _same_device(x, ("table", table))
+    if x.dim() == 3 and x.shape[0] != 1:
+        raise RuntimeError(f"{name} gathers one [N, C] slab; got shape {tuple(x.shape)}")
+    if x.dim() not in (2, 3):
+        raise RuntimeError(f"x must be [N, C] or [1, N, C], got {tuple(x.shape)}")
+    shape = (table.numel(), x.shape[-1]) if x.dim() == 2 else (1, table.numel(), x.shape[-1])
+    return n_src, shape
+
+
+def window_gather(x: torch.Tensor, table: torch.Tensor, out: torch.Tensor = None) -> torch.Tensor:
+    """out[j] = x[table[j]] for 0 <= table[j] < N, else a +0.0 row."""
+    n_src, shape = _gather_args(x, table, "window_gather")
+    o = _out_like(out, shape, x.device, "out")
+    lib = _lib.load()
+    with torch.cuda.device(x.device):
+        _lib.check(lib.lwg_window_gather(_ptr(x), n_src, x.shape[-1], _ptr(table), table.numel(),
+                                         _ptr(o), _stream(x.device)))
+    return o
+
+
+def norm_gather(x: torch.Tensor, table: torch.Tensor, eps: float = EPS,
+                out: torch.Tensor = None) -> torch.Tensor:
+    """out[j] = LayerNorm(x[table[j]]) for 0 <= table[j] < N, else a +0.0 row;
+    the normalised tensor itself is never written."""
+    n_src, shape = _gather_args(x, table, "norm_gather")
+    o = _out_like(out, shape, x.device, "out")
+    lib = _lib.load()
+    with torch.cuda.device(x.device):
+        _lib.check(lib.lwg_norm_gather(_ptr(x), n_src, x.shape[-1], _ptr(table), table.numel(),
+                                       float(eps), _ptr(o), _stream(x.device)))
+    return o
+
+
+class Prepared:
+    """A checked, pre-marshalled call of one C entry point on fixed tensors and a
+    fixed stream (the device's current stream when prepared). Calling it only
+    crosses the C ABI, which repeats its own argument checks; use it where the
+    per-call Python checks would cost more than the kernel (timed loops).
+    The tensors must stay alive and unchanged in shape while it is used."""
+
+    def __init__(self, fn, args, keep):
+        self._fn, self._args, self._keep = fn, args, keep
+
+    def __call__(self) -> None:
+        _lib.check(self._fn(*self._args))
+
+
+def prepare(op: str, *tensors, eps: float = EPS, grid=None, window=None, shift=(0, 0, 0)) -> Prepared:
+    """Prepare ``op`` on the given tensors, checked as the plain functions check them:
+      prepare("ln_fixed", x, y)
+      prepare("add_ln", branch, residual, residual_out, y)
+      prepare("window_index_build", table, grid=..., window=..., shift=...)
+      prepare("window_gather", x, table, out)
+      prepare("norm_gather", x, table, out)"""
+    lib = _lib.load()
+    if op == "ln_fixed":
+        x, y = tensors
+        rows = _rows(x, "x")
+        _out_like(y, x.shape, x.device, "y")
+        dev = x.device
+        fn, args = lib.lwg_ln_fixed, (_ptr(x), _ptr(y), rows, x.shape[-1], float(eps), _stream(dev))
+    elif op == "add_ln":
+        b, r, ro, y = tensors
+        rows = _rows(r, "residual")
+        _rows(b, "branch")
+        if tuple(b.shape) != tuple(r.shape):
+            raise RuntimeError("branch and residual shapes differ")
+        _out_like(ro, r.shape, r.device, "residual_out")
+        _out_like(y, r.shape, r.device, "y")
+        dev = r.device
+        fn, args = lib.lwg_add_ln, (_ptr(b), _ptr(r), _ptr(ro), _ptr(y), rows, r.shape[-1], float(eps),
+                                    _stream(dev))
+    elif op == "window_index_build":
+        (table,) = tensors
+        g, w, s = _triple(grid, "grid"), _triple(window, "window"), _triple(shift, "shift")
+        if table.dtype != torch.int32 or table.device.type != "cuda" or not table.is_contiguous():
+            raise RuntimeError("table must be a contiguous int32 GPU tensor")
+        dev = table.device
+        fn, args = lib.lwg_window_index_build, (*g, *w, *s, _ptr(table), table.numel(), _stream(dev))
+    elif op in ("window_gather", "norm_gather"):
+        x, table, out = tensors
+        n_src, shape = _gather_args(x, table, op)
+        _out_like(out, shape, x.device, "out")
+        dev = x.device
+        if op == "window_gather":
+            fn, args = lib.lwg_window_gather, (_ptr(x), n_src, x.shape[-1], _ptr(table), table.numel(),
+                                               _ptr(out), _stream(dev))
+        else:
+            fn, args = lib.lwg_norm_gather, (_ptr(x), n_src, x.shape[-1], _ptr(table), table.numel(),
+                                             float(eps), _ptr(out), _stream(dev))
+    else:
+        raise ValueError(f"unknown op {op!r}")
+    return Prepared(fn, args, tensors)
+
+
+__all__ += ["Prepared", "prepare"]

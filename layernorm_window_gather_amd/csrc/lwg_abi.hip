@@ -1,0 +1,236 @@
+// extern "C" entry points declared in include/lwg.h: host-side argument checks,
+// then one launch on the caller's stream. Nothing here allocates, frees or
+// synchronises. The checks follow the contract style of the page "PyTorch + HIP
+// custom fused operator" (Hygon DCU practice series), section 6: refuse bad
+// input before launching, return early on empty input, use the caller's
+// stream, and turn a launch error into an error result.
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include <hip/hip_runtime.h>
+
+#include "lwg.h"
+#include "lwg_launch.h"
+
+#define LWG_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int32_t fail(lwg_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+int32_t ok() {
+    g_last_error.clear();
+    return LWG_OK;
+}
+
+int32_t hip_result(hipError_t e, const char* what) {
+    if (e != hipSuccess)
+        return fail(LWG_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// [a, a+na) and [b, b+nb) share a byte.
+bool overlap(const void* a, uint64_t na, const void* b, uint64_t nb) {
+    const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+    return pa < pb + nb && pb < pa + na;
+}
+
+// Same buffer (exact alias) or disjoint; a partial overlap is an error.
+bool same_or_disjoint(const void* a, const void* b, uint64_t n) {
+    return a == b || !overlap(a, n, b, n);
+}
+
+int32_t check_width(const char* fn, int32_t C) {
+    if (C != 192 && C != 384)
+        return fail(LWG_ERR_UNSUPPORTED_WIDTH, "%s: C=%d is not served (only 192 and 384)", fn, C);
+    return LWG_OK;
+}
+
+int32_t check_eps(const char* fn, double eps) {
+    if (!(std::isfinite(eps) && eps > 0.0))
+        return fail(LWG_ERR_INVALID_ARGUMENT, "%s: eps must be finite and > 0 (got %g)", fn, eps);
+    return LWG_OK;
+}
+
+int32_t check_rows(const char* fn, const char* name, int64_t rows) {
+    if (rows < 0 || rows > INT32_MAX)
+        return fail(LWG_ERR_INVALID_ARGUMENT, "%s: %s=%lld must be in [0, 2^31-1]", fn, name,
+                    static_cast<long long>(rows));
+    return LWG_OK;
+}
+
+int32_t check_tensor(const char* fn, const char* name, const void* p) {
+    if (p == nullptr) return fail(LWG_ERR_INVALID_ARGUMENT, "%s: %s is NULL", fn, name);
+    if (!aligned16(p)) return fail(LWG_ERR_MISALIGNED, "%s: %s is not 16-byte aligned", fn, name);
+    return LWG_OK;
+}
+
+// Padded extent of one axis, or -1 when the inputs are out of range.
+int64_t padded(int64_t extent, int64_t window) {
+    if (extent < 0 || window < 1) return -1;
+    return (extent + window - 1) / window * window;
+}
+
+}  // namespace
+
+LWG_EXPORT int32_t lwg_abi_version(void) { return LWG_ABI_VERSION; }
+
+LWG_EXPORT const char* lwg_last_error(void) { return g_last_error.c_str(); }
+
+LWG_EXPORT const char* lwg_status_string(int32_t status) {
+    switch (status) {
+        case LWG_OK: return "LWG_OK";
+        case LWG_ERR_INVALID_ARGUMENT: return "LWG_ERR_INVALID_ARGUMENT";
+        case LWG_ERR_UNSUPPORTED_WIDTH: return "LWG_ERR_UNSUPPORTED_WIDTH";
+        case LWG_ERR_MISALIGNED: return "LWG_ERR_MISALIGNED";
+        case LWG_ERR_ALIASING: return "LWG_ERR_ALIASING";
+        case LWG_ERR_SIZE_MISMATCH: return "LWG_ERR_SIZE_MISMATCH";
+        case LWG_ERR_HIP: return "LWG_ERR_HIP";
+        default: return "LWG_ERR_UNKNOWN";
+    }
+}
+
+LWG_EXPORT int32_t lwg_ln_fixed(const void* x, void* y, int64_t rows, int32_t C, double eps,
+                                void* stream) {
+    static const char* fn = "lwg_ln_fixed";
+    int32_t st;
+    if ((st = check_width(fn, C)) || (st = check_eps(fn, eps)) || (st = check_rows(fn, "rows", rows)))
+        return st;
+    if (rows == 0) return ok();
+    if ((st = check_tensor(fn, "x", x)) || (st = check_tensor(fn, "y", y))) return st;
+    const uint64_t bytes = static_cast<uint64_t>(rows) * C * 2;
+    if (!same_or_disjoint(x, y, bytes))
+        return fail(LWG_ERR_ALIASING, "%s: y partially overlaps x (only y == x is allowed)", fn);
+    return hip_result(lwg::launch_ln_fixed(x, y, rows, C, eps, static_cast<hipStream_t>(stream)), fn);
+}
+
+LWG_EXPORT int32_t lwg_add_ln(const void* branch, const void* residual, void* residual_out,
+                              void* y, int64_t rows, int32_t C, double eps, void* stream) {
+    static const char* fn = "lwg_add_ln";
+    int32_t st;
+    if ((st = check_width(fn, C)) || (st = check_eps(fn, eps)) || (st = check_rows(fn, "rows", rows)))
+        return st;
+    if (rows == 0) return ok();
+    if ((st = check_tensor(fn, "branch", branch)) || (st = check_tensor(fn, "residual", residual)) ||
+        (st = check_tensor(fn, "residual_out", residual_out)) || (st = check_tensor(fn, "y", y)))
+        return st;
+    const uint64_t bytes = static_cast<uint64_t>(rows) * C * 2;
+    if (overlap(y, bytes, residual_out, bytes))
+        return fail(LWG_ERR_ALIASING, "%s: y and residual_out overlap", fn);
+    if (!same_or_disjoint(residual_out, residual, bytes) || !same_or_disjoint(residual_out, branch, bytes) ||
+        !same_or_disjoint(y, residual, bytes) || !same_or_disjoint(y, branch, bytes))
+        return fail(LWG_ERR_ALIASING,
+                    "%s: an output partially overlaps an input (only exact in-place aliasing is allowed)", fn);
+    return hip_result(lwg::launch_add_ln(branch, residual, residual_out, y, rows, C, eps,
+                                         static_cast<hipStream_t>(stream)),
+                      fn);
+}
+
+LWG_EXPORT int64_t lwg_window_token_count(int32_t Z, int32_t H, int32_t W, int32_t wz, int32_t wh,
+                                          int32_t ww) {
+    const int64_t zp = padded(Z, wz), hp = padded(H, wh), wp = padded(W, ww);
+    if (zp < 0 || hp < 0 || wp < 0) return -1;
+    // each padded extent is below 2^32, so check the product stepwise
+    const int64_t zh = zp * hp;
+    if (zh > INT32_MAX || (wp != 0 && zh > INT32_MAX / wp)) return -1;
+    const int64_t n = zh * wp;
+    return n > INT32_MAX ? -1 : n;
+}
+
+LWG_EXPORT int32_t lwg_window_index_build(int32_t Z, int32_t H, int32_t W, int32_t wz, int32_t wh,
+                                          int32_t ww, int32_t sz, int32_t sh, int32_t sw,
+                                          int32_t* table, int64_t table_len, void* stream) {
+    static const char* fn = "lwg_window_index_build";
+    if (Z < 0 || H < 0 || W < 0)
+        return fail(LWG_ERR_INVALID_ARGUMENT, "%s: grid extents must be >= 0 (got %d,%d,%d)", fn, Z, H, W);
+    if (wz < 1 || wh < 1 || ww < 1)
+        return fail(LWG_ERR_INVALID_ARGUMENT, "%s: window extents must be >= 1 (got %d,%d,%d)", fn, wz, wh, ww);
+    if (sz < 0 || sh < 0 || sw < 0)
+        return fail(LWG_ERR_INVALID_ARGUMENT, "%s: shifts must be >= 0 (got %d,%d,%d)", fn, sz, sh, sw);
+    const int64_t tokens = static_cast<int64_t>(Z) * H * W;
+    if (tokens > INT32_MAX)
+        return fail(LWG_ERR_INVALID_ARGUMENT, "%s: grid holds more than 2^31-1 tokens", fn);
+    const int64_t m = lwg_window_token_count(Z, H, W, wz, wh, ww);
+    if (m < 0)
+        return fail(LWG_ERR_INVALID_ARGUMENT, "%s: padded grid holds more than 2^31-1 rows", fn);
+    if (table_len != m)
+        return fail(LWG_ERR_SIZE_MISMATCH, "%s: table_len=%lld but the window token count is %lld", fn,
+                    static_cast<long long>(table_len), static_cast<long long>(m));
+    if (m == 0) return ok();
+    if (table == nullptr) return fail(LWG_ERR_INVALID_ARGUMENT, "%s: table is NULL", fn);
+    if ((reinterpret_cast<uintptr_t>(table) & 3u) != 0)
+        return fail(LWG_ERR_MISALIGNED, "%s: table is not 4-byte aligned", fn);
+    lwg::WindowGeometry g;
+    g.Z = Z; g.H = H; g.W = W;
+    g.wz = wz; g.wh = wh; g.ww = ww;
+    g.Zp = static_cast<int32_t>(padded(Z, wz));
+    g.Hp = static_cast<int32_t>(padded(H, wh));
+    g.Wp = static_cast<int32_t>(padded(W, ww));
+    g.sz = sz % g.Zp; g.sh = sh % g.Hp; g.sw = sw % g.Wp;
+    g.nbh = g.Hp / wh; g.nbw = g.Wp / ww;
+    g.win_tokens = wz * wh * ww;
+    g.rows = static_cast<int32_t>(m);
+    return hip_result(lwg::launch_window_index(g, table, static_cast<hipStream_t>(stream)), fn);
+}
+
+namespace {
+
+int32_t check_gather(const char* fn, const void* x, int64_t n_src, int32_t C, const int32_t* table,
+                     int64_t n_out, const void* out) {
+    int32_t st;
+    if ((st = check_width(fn, C)) || (st = check_rows(fn, "n_src", n_src)) ||
+        (st = check_rows(fn, "n_out", n_out)))
+        return st;
+    if (n_out == 0) return LWG_OK;
+    if (n_src > 0 && (st = check_tensor(fn, "x", x))) return st;
+    if ((st = check_tensor(fn, "out", out))) return st;
+    if (table == nullptr) return fail(LWG_ERR_INVALID_ARGUMENT, "%s: table is NULL", fn);
+    if ((reinterpret_cast<uintptr_t>(table) & 3u) != 0)
+        return fail(LWG_ERR_MISALIGNED, "%s: table is not 4-byte aligned", fn);
+    const uint64_t out_bytes = static_cast<uint64_t>(n_out) * C * 2;
+    if (n_src > 0 && overlap(out, out_bytes, x, static_cast<uint64_t>(n_src) * C * 2))
+        return fail(LWG_ERR_ALIASING, "%s: out overlaps x", fn);
+    if (overlap(out, out_bytes, table, static_cast<uint64_t>(n_out) * 4))
+        return fail(LWG_ERR_ALIASING, "%s: out overlaps table", fn);
+    return LWG_OK;
+}
+
+}  // namespace
+
+LWG_EXPORT int32_t lwg_window_gather(const void* x, int64_t n_src, int32_t C, const int32_t* table,
+                                     int64_t n_out, void* out, void* stream) {
+    static const char* fn = "lwg_window_gather";
+    int32_t st = check_gather(fn, x, n_src, C, table, n_out, out);
+    if (st) return st;
+    if (n_out == 0) return ok();
+    return hip_result(lwg::launch_window_gather(x, n_src, C, table, n_out, out,
+                                                static_cast<hipStream_t>(stream)),
+                      fn);
+}
+
+LWG_EXPORT int32_t lwg_norm_gather(const void* x, int64_t n_src, int32_t C, const int32_t* table,
+                                   int64_t n_out, double eps, void* out, void* stream) {
+    static const char* fn = "lwg_norm_gather";
+    int32_t st = check_eps(fn, eps);
+    if (st) return st;
+    if ((st = check_gather(fn, x, n_src, C, table, n_out, out))) return st;
+    if (n_out == 0) return ok();
+    return hip_result(lwg::launch_norm_gather(x, n_src, C, table, n_out, eps, out,
+                                              static_cast<hipStream_t>(stream)),
+                      fn);
+}

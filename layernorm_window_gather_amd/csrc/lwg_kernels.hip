@@ -1,0 +1,381 @@
+// Row kernels for gfx950 (CDNA4, wave64): fixed-width LayerNorm, residual add +
+// LayerNorm, shifted-window index tables, window gather and fused norm-gather.
+//
+// What is computed follows the page "Pangu-Weather inference optimisation on
+// Hygon BW1000 (gfx936)" (l189.com/news/2144533):
+//   section 3 -- LayerNorm over rows of width 192 or 384, FP16 in and out, no affine;
+//   section 4 -- residual add whose FP16 rounding is kept, then LayerNorm of it;
+//   section 5 -- INT32 window index tables (-1 = padding row = zeros), a gather
+//                driven by them, and the norm-gather fusion.
+// How it is computed is designed for CDNA4 rather than taken from that page
+// (which used one wave per row and __half2 moves on gfx936):
+//   * Every access is a 16-byte (8 x binary16) vector load or store. A row of C
+//     values is split over LPR = C/(8K) consecutive lanes holding K chunks each;
+//     chunk k of a lane sits at column chunk (lane % LPR) + k*LPR, so one wave
+//     instruction reads 64/LPR rows x LPR*16 contiguous bytes (whole 128-byte
+//     lines), and the K instructions of a wave cover 64/LPR full rows.
+//   * Row statistics are reduced across the LPR lanes of a row with DPP
+//     (quad_perm / row_half_mirror / row_mirror), no LDS and no barriers.
+//   * Statistics and the normalisation run in binary64: CDNA4 issues FP64 vector
+//     adds and FMAs at the same per-lane rate as plain FP32, and binary64 makes
+//     each output the correctly rounded binary16 of the exact LayerNorm in
+//     practice, where FP32 arithmetic flips about 1e-4 of outputs by one ulp.
+//     The final binary64 -> binary16 rounding goes through a round-to-odd
+//     binary32 intermediate, which makes the two-step conversion exact-once.
+//   * All kernels are stateless and row-local: no atomics, no shared memory.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lwg_launch.h"
+
+namespace lwg {
+namespace {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kBlock = 256;  // 4 waves per workgroup
+
+// ---------------------------------------------------------------------------
+// Lane geometry of a row tile
+
+template <int C, int K>
+struct Tile {
+    static_assert(C % (8 * K) == 0, "a lane holds K whole 16-byte chunks");
+    static constexpr int kChunks = C / 8;              // 16-byte chunks per row
+    static constexpr int kLanes = kChunks / K;          // lanes sharing one row
+    static constexpr int kRowsPerWave = 64 / kLanes;    // rows per wave instruction
+    static constexpr int kValues = 8 * K;               // binary16 values per lane
+    static_assert(kLanes == 2 || kLanes == 4 || kLanes == 8 || kLanes == 16,
+                  "row groups must sit inside one 16-lane DPP row");
+};
+
+// Chunks per lane for each width: both widths use 3 chunks (24 values) per
+// lane, i.e. 8 lanes per row at C=192 and 16 lanes per row at C=384.
+template <int C> struct Config { static constexpr int K = 3; };
+
+// ---------------------------------------------------------------------------
+// Cross-lane sums inside a row group, with DPP
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const uint64_t lo = dpp_u32<CTRL>(static_cast<uint32_t>(b));
+    const uint64_t hi = dpp_u32<CTRL>(static_cast<uint32_t>(b >> 32));
+    return __builtin_bit_cast(double, (hi << 32) | lo);
+}
+
+// Sum over the LPR consecutive lanes of a row group; every lane of the group
+// receives the same bits (each step adds a lane's value to its partner's, and
+// IEEE addition commutes).
+template <int LPR>
+__device__ __forceinline__ double group_sum(double v) {
+    v += dpp_f64<0xB1>(v);                          // quad_perm [1,0,3,2]: lane ^ 1
+    if constexpr (LPR >= 4) v += dpp_f64<0x4E>(v);  // quad_perm [2,3,0,1]: lane ^ 2
+    if constexpr (LPR >= 8) v += dpp_f64<0x141>(v); // row_half_mirror: quad <-> quad
+    if constexpr (LPR >= 16) v += dpp_f64<0x140>(v);// row_mirror: 8 lanes <-> 8 lanes
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// Conversions
+
+__device__ __forceinline__ void unpack8(const uint4& c, double* out) {
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const half2_t h = __builtin_bit_cast(half2_t, w[i]);
+        out[2 * i] = static_cast<double>(static_cast<float>(h.x));
+        out[2 * i + 1] = static_cast<double>(static_cast<float>(h.y));
+    }
+}
+
+// binary64 -> binary16, rounded once to nearest-even. The binary64 value is
+// first cut to binary32 with round-to-odd (truncate the 29 extra significand
+// bits, set the binary32 last bit if any of them was set); binary32 keeps 13
+// bits beyond binary16, so the following nearest-even conversion sees the same
+// rounding decision as a direct one. NaN stays NaN, +-Inf and +-0 are kept.
+// Magnitudes below the binary32 normal range are far below half the smallest
+// binary16 subnormal and go to +-0 either way.
+__device__ __forceinline__ _Float16 to_half_rn(double y) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, y);
+    const uint32_t lo = static_cast<uint32_t>(b);
+    const uint32_t sticky = ((lo & 0x1FFFFFFFu) + 0x1FFFFFFFu) & 0x20000000u;
+    const uint64_t t = (b & 0xFFFFFFFFE0000000ull) | sticky;
+    const float f = static_cast<float>(__builtin_bit_cast(double, t));  // exact
+    return static_cast<_Float16>(f);
+}
+
+__device__ __forceinline__ uint32_t pack2(double a, double b) {
+    half2_t h;
+    h.x = to_half_rn(a);
+    h.y = to_half_rn(b);
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+// ---------------------------------------------------------------------------
+// Row math
+
+// FP16 residual of section 4: residual + branch rounded once to binary16. The
+// packed binary16 add computes the exact sum rounded to nearest-even.
+template <int K>
+__device__ __forceinline__ void residual_add(const uint4 (&branch)[K], uint4 (&res)[K]) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        uint32_t r[4] = {res[k].x, res[k].y, res[k].z, res[k].w};
+        const uint32_t b[4] = {branch[k].x, branch[k].y, branch[k].z, branch[k].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const half2_t s = __builtin_bit_cast(half2_t, r[i]) + __builtin_bit_cast(half2_t, b[i]);
+            r[i] = __builtin_bit_cast(uint32_t, s);
+        }
+        res[k] = make_uint4(r[0], r[1], r[2], r[3]);
+    }
+}
+
+// LayerNorm of the row whose 1/LPR share this lane holds in v (section 3):
+// mean, biased variance of the deviations (two passes over registers), then
+// (x - mean) / sqrt(var + eps) rounded to binary16, written back into v.
+// Every kernel that normalises a row calls this same function with the same
+// (C, K), so their outputs agree bit for bit.
+template <int C, int K>
+__device__ __forceinline__ void layer_norm_lane(uint4 (&v)[K], double eps) {
+    using T = Tile<C, K>;
+    double x[T::kValues];
+#pragma unroll
+    for (int k = 0; k < K; ++k) unpack8(v[k], x + 8 * k);
+
+    double s0 = 0.0, s1 = 0.0;
+#pragma unroll
+    for (int i = 0; i < T::kValues; i += 2) {
+        s0 += x[i];
+        s1 += x[i + 1];
+    }
+    const double mean = group_sum<T::kLanes>(s0 + s1) / static_cast<double>(C);
+
+    double q0 = 0.0, q1 = 0.0;
+#pragma unroll
+    for (int i = 0; i < T::kValues; i += 2) {
+        const double d0 = x[i] - mean, d1 = x[i + 1] - mean;
+        q0 = __builtin_fma(d0, d0, q0);
+        q1 = __builtin_fma(d1, d1, q1);
+    }
+    const double var = group_sum<T::kLanes>(q0 + q1) / static_cast<double>(C);
+    const double rstd = 1.0 / __builtin_sqrt(var + eps);
+
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const double* xk = x + 8 * k;
+        v[k] = make_uint4(pack2((xk[0] - mean) * rstd, (xk[1] - mean) * rstd),
+                          pack2((xk[2] - mean) * rstd, (xk[3] - mean) * rstd),
+                          pack2((xk[4] - mean) * rstd, (xk[5] - mean) * rstd),
+                          pack2((xk[6] - mean) * rstd, (xk[7] - mean) * rstd));
+    }
+}
+
+// Row handled by this lane and the lane's position inside the row group.
+template <int C, int K>
+__device__ __forceinline__ int64_t tile_row(int& sub) {
+    using T = Tile<C, K>;
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = static_cast<int64_t>(blockIdx.x) * (kBlock / 64) + (threadIdx.x >> 6);
+    sub = lane % T::kLanes;
+    return wave * T::kRowsPerWave + lane / T::kLanes;
+}
+
+template <int K>
+__device__ __forceinline__ void zero(uint4 (&v)[K]) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) v[k] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// ---------------------------------------------------------------------------
+// Kernels
+
+// y may alias x: a lane reads all of its chunks before the row statistics
+// exist, and writes only the chunks it read.
+template <int C, int K>
+__global__ __launch_bounds__(kBlock) void ln_fixed_kernel(const uint4* x, uint4* y,
+                                                          int64_t rows, double eps) {
+    using T = Tile<C, K>;
+    int sub;
+    const int64_t row = tile_row<C, K>(sub);
+    const bool live = row < rows;
+    const int64_t base = row * T::kChunks + sub;
+    uint4 v[K];
+    zero(v);
+    if (live) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) v[k] = x[base + k * T::kLanes];
+    }
+    layer_norm_lane<C, K>(v, eps);
+    if (live) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) y[base + k * T::kLanes] = v[k];
+    }
+}
+
+template <int C, int K>
+__global__ __launch_bounds__(kBlock) void add_ln_kernel(const uint4* branch, const uint4* residual,
+                                                        uint4* residual_out, uint4* y,
+                                                        int64_t rows, double eps) {
+    using T = Tile<C, K>;
+    int sub;
+    const int64_t row = tile_row<C, K>(sub);
+    const bool live = row < rows;
+    const int64_t base = row * T::kChunks + sub;
+    uint4 b[K], r[K];
+    zero(b);
+    zero(r);
+    if (live) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            b[k] = branch[base + k * T::kLanes];
+            r[k] = residual[base + k * T::kLanes];
+        }
+    }
+    residual_add<K>(b, r);
+    if (live) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) residual_out[base + k * T::kLanes] = r[k];
+    }
+    layer_norm_lane<C, K>(r, eps);
+    if (live) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) y[base + k * T::kLanes] = r[k];
+    }
+}
+
+// Output-major gather: lane group j reads table[j] and, for a valid entry,
+// the whole source row; padding and out-of-range entries read nothing and
+// store +0.0 (LayerNorm of a zero row is exactly +0.0 as well).
+template <int C, int K, bool kNorm>
+__global__ __launch_bounds__(kBlock) void gather_kernel(const uint4* __restrict__ x, int64_t n_src,
+                                                        const int32_t* __restrict__ table,
+                                                        int64_t n_out, uint4* __restrict__ out,
+                                                        double eps) {
+    using T = Tile<C, K>;
+    int sub;
+    const int64_t j = tile_row<C, K>(sub);
+    const bool live = j < n_out;
+    const int32_t t = live ? table[j] : -1;
+    const bool valid = t >= 0 && static_cast<int64_t>(t) < n_src;
+    const int64_t src = static_cast<int64_t>(t) * T::kChunks + sub;
+    uint4 v[K];
+    zero(v);
+    if (valid) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) v[k] = x[src + k * T::kLanes];
+    }
+    if constexpr (kNorm) layer_norm_lane<C, K>(v, eps);
+    if (live) {
+        const int64_t dst = j * T::kChunks + sub;
+#pragma unroll
+        for (int k = 0; k < K; ++k) out[dst + k * T::kLanes] = v[k];
+    }
+}
+
+// One thread per table entry. Entry j = window * win_tokens + t; windows are
+// row-major over (bz, bh, bw), tokens row-major over (dz, dh, dw). Gathered
+// position p = (b*w + d) reads padded position (p + s) mod padded extent; a
+// position past the real grid on any axis is padding (-1).
+__global__ __launch_bounds__(kBlock) void window_index_kernel(WindowGeometry g, int32_t* table) {
+    const int32_t j = static_cast<int32_t>(blockIdx.x) * kBlock + static_cast<int32_t>(threadIdx.x);
+    if (j >= g.rows) return;
+    const int32_t wid = j / g.win_tokens;
+    const int32_t t = j - wid * g.win_tokens;
+    const int32_t bw = wid % g.nbw;
+    const int32_t bzh = wid / g.nbw;
+    const int32_t bh = bzh % g.nbh;
+    const int32_t bz = bzh / g.nbh;
+    const int32_t dw = t % g.ww;
+    const int32_t dzh = t / g.ww;
+    const int32_t dh = dzh % g.wh;
+    const int32_t dz = dzh / g.wh;
+    // b*w + d < padded extent and s < padded extent: the sum stays below 2^32
+    int64_t qz = static_cast<int64_t>(bz) * g.wz + dz + g.sz;
+    int64_t qh = static_cast<int64_t>(bh) * g.wh + dh + g.sh;
+    int64_t qw = static_cast<int64_t>(bw) * g.ww + dw + g.sw;
+    if (qz >= g.Zp) qz -= g.Zp;
+    if (qh >= g.Hp) qh -= g.Hp;
+    if (qw >= g.Wp) qw -= g.Wp;
+    table[j] = (qz < g.Z && qh < g.H && qw < g.W)
+                   ? static_cast<int32_t>((qz * g.H + qh) * g.W + qw)
+                   : -1;
+}
+
+// ---------------------------------------------------------------------------
+// Launch helpers
+
+template <int C>
+unsigned grid_for(int64_t rows) {
+    using T = Tile<C, Config<C>::K>;
+    const int64_t tiles = (rows + T::kRowsPerWave - 1) / T::kRowsPerWave;
+    return static_cast<unsigned>((tiles + (kBlock / 64) - 1) / (kBlock / 64));
+}
+
+template <int C>
+hipError_t ln_fixed_c(const void* x, void* y, int64_t rows, double eps, hipStream_t s) {
+    constexpr int K = Config<C>::K;
+    ln_fixed_kernel<C, K><<<grid_for<C>(rows), kBlock, 0, s>>>(
+        static_cast<const uint4*>(x), static_cast<uint4*>(y), rows, eps);
+    return hipGetLastError();
+}
+
+template <int C>
+hipError_t add_ln_c(const void* b, const void* r, void* ro, void* y, int64_t rows, double eps,
+                    hipStream_t s) {
+    constexpr int K = Config<C>::K;
+    add_ln_kernel<C, K><<<grid_for<C>(rows), kBlock, 0, s>>>(
+        static_cast<const uint4*>(b), static_cast<const uint4*>(r), static_cast<uint4*>(ro),
+        static_cast<uint4*>(y), rows, eps);
+    return hipGetLastError();
+}
+
+template <int C, bool kNorm>
+hipError_t gather_c(const void* x, int64_t n_src, const int32_t* table, int64_t n_out, double eps,
+                    void* out, hipStream_t s) {
+    constexpr int K = Config<C>::K;
+    gather_kernel<C, K, kNorm><<<grid_for<C>(n_out), kBlock, 0, s>>>(
+        static_cast<const uint4*>(x), n_src, table, n_out, static_cast<uint4*>(out), eps);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_ln_fixed(const void* x, void* y, int64_t rows, int32_t C, double eps,
+                           hipStream_t stream) {
+    return C == 192 ? ln_fixed_c<192>(x, y, rows, eps, stream)
+                    : ln_fixed_c<384>(x, y, rows, eps, stream);
+}
+
+hipError_t launch_add_ln(const void* branch, const void* residual, void* residual_out, void* y,
+                         int64_t rows, int32_t C, double eps, hipStream_t stream) {
+    return C == 192 ? add_ln_c<192>(branch, residual, residual_out, y, rows, eps, stream)
+                    : add_ln_c<384>(branch, residual, residual_out, y, rows, eps, stream);
+}
+
+hipError_t launch_window_index(const WindowGeometry& g, int32_t* table, hipStream_t stream) {
+    const unsigned grid = static_cast<unsigned>((static_cast<int64_t>(g.rows) + kBlock - 1) / kBlock);
+    window_index_kernel<<<grid, kBlock, 0, stream>>>(g, table);
+    return hipGetLastError();
+}
+
+hipError_t launch_window_gather(const void* x, int64_t n_src, int32_t C, const int32_t* table,
+                                int64_t n_out, void* out, hipStream_t stream) {
+    return C == 192 ? gather_c<192, false>(x, n_src, table, n_out, 0.0, out, stream)
+                    : gather_c<384, false>(x, n_src, table, n_out, 0.0, out, stream);
+}
+
+hipError_t launch_norm_gather(const void* x, int64_t n_src, int32_t C, const int32_t* table,
+                              int64_t n_out, double eps, void* out, hipStream_t stream) {
+    return C == 192 ? gather_c<192, true>(x, n_src, table, n_out, eps, out, stream)
+                    : gather_c<384, true>(x, n_src, table, n_out, eps, out, stream);
+}
+
+}  // namespace lwg
