@@ -32,8 +32,29 @@ namespace lwg {
 namespace {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t chunk_t __attribute__((ext_vector_type(4)));  // 16 bytes = 8 x binary16
 
 constexpr int kBlock = 256;  // 4 waves per workgroup
+
+// Memory hints of a kernel instance: non-temporal loads / stores (the `nt` bit
+// on global_load/global_store: stream through the caches without keeping lines).
+template <bool NTL, bool NTS>
+struct Hints {
+    static constexpr bool kNtLoad = NTL;
+    static constexpr bool kNtStore = NTS;
+};
+
+template <class H>
+__device__ __forceinline__ chunk_t load16(const chunk_t* p) {
+    if constexpr (H::kNtLoad) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+
+template <class H>
+__device__ __forceinline__ void store16(chunk_t* p, chunk_t v) {
+    if constexpr (H::kNtStore) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
 
 // ---------------------------------------------------------------------------
 // Lane geometry of a row tile
@@ -49,9 +70,6 @@ struct Tile {
                   "row groups must sit inside one 16-lane DPP row");
 };
 
-// Chunks per lane for each width: both widths use 3 chunks (24 values) per
-// lane, i.e. 8 lanes per row at C=192 and 16 lanes per row at C=384.
-template <int C> struct Config { static constexpr int K = 3; };
 
 // ---------------------------------------------------------------------------
 // Cross-lane sums inside a row group, with DPP
@@ -85,7 +103,7 @@ __device__ __forceinline__ double group_sum(double v) {
 // ---------------------------------------------------------------------------
 // Conversions
 
-__device__ __forceinline__ void unpack8(const uint4& c, double* out) {
+__device__ __forceinline__ void unpack8(const chunk_t& c, double* out) {
     const uint32_t w[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -124,7 +142,7 @@ __device__ __forceinline__ uint32_t pack2(double a, double b) {
 // FP16 residual of section 4: residual + branch rounded once to binary16. The
 // packed binary16 add computes the exact sum rounded to nearest-even.
 template <int K>
-__device__ __forceinline__ void residual_add(const uint4 (&branch)[K], uint4 (&res)[K]) {
+__device__ __forceinline__ void residual_add(const chunk_t (&branch)[K], chunk_t (&res)[K]) {
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         uint32_t r[4] = {res[k].x, res[k].y, res[k].z, res[k].w};
@@ -134,7 +152,7 @@ __device__ __forceinline__ void residual_add(const uint4 (&branch)[K], uint4 (&r
             const half2_t s = __builtin_bit_cast(half2_t, r[i]) + __builtin_bit_cast(half2_t, b[i]);
             r[i] = __builtin_bit_cast(uint32_t, s);
         }
-        res[k] = make_uint4(r[0], r[1], r[2], r[3]);
+        res[k] = chunk_t{r[0], r[1], r[2], r[3]};
     }
 }
 
@@ -144,7 +162,7 @@ __device__ __forceinline__ void residual_add(const uint4 (&branch)[K], uint4 (&r
 // Every kernel that normalises a row calls this same function with the same
 // (C, K), so their outputs agree bit for bit.
 template <int C, int K>
-__device__ __forceinline__ void layer_norm_lane(uint4 (&v)[K], double eps) {
+__device__ __forceinline__ void layer_norm_lane(chunk_t (&v)[K], double eps) {
     using T = Tile<C, K>;
     double x[T::kValues];
 #pragma unroll
@@ -171,112 +189,126 @@ __device__ __forceinline__ void layer_norm_lane(uint4 (&v)[K], double eps) {
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         const double* xk = x + 8 * k;
-        v[k] = make_uint4(pack2((xk[0] - mean) * rstd, (xk[1] - mean) * rstd),
-                          pack2((xk[2] - mean) * rstd, (xk[3] - mean) * rstd),
-                          pack2((xk[4] - mean) * rstd, (xk[5] - mean) * rstd),
-                          pack2((xk[6] - mean) * rstd, (xk[7] - mean) * rstd));
+        v[k] = chunk_t{pack2((xk[0] - mean) * rstd, (xk[1] - mean) * rstd),
+                       pack2((xk[2] - mean) * rstd, (xk[3] - mean) * rstd),
+                       pack2((xk[4] - mean) * rstd, (xk[5] - mean) * rstd),
+                       pack2((xk[6] - mean) * rstd, (xk[7] - mean) * rstd)};
     }
 }
 
-// Row handled by this lane and the lane's position inside the row group.
-template <int C, int K>
-__device__ __forceinline__ int64_t tile_row(int& sub) {
-    using T = Tile<C, K>;
-    const int lane = threadIdx.x & 63;
-    const int64_t wave = static_cast<int64_t>(blockIdx.x) * (kBlock / 64) + (threadIdx.x >> 6);
-    sub = lane % T::kLanes;
-    return wave * T::kRowsPerWave + lane / T::kLanes;
-}
-
 template <int K>
-__device__ __forceinline__ void zero(uint4 (&v)[K]) {
+__device__ __forceinline__ void zero(chunk_t (&v)[K]) {
 #pragma unroll
-    for (int k = 0; k < K; ++k) v[k] = make_uint4(0u, 0u, 0u, 0u);
+    for (int k = 0; k < K; ++k) v[k] = chunk_t{0u, 0u, 0u, 0u};
 }
 
 // ---------------------------------------------------------------------------
 // Kernels
+//
+// Wave w of the grid handles row tiles w, w + (waves in the grid), ...; a tile
+// is the kRowsPerWave rows one wave covers. The loop bound is the same for every
+// lane of a wave, so the DPP reductions always run with the whole wave active.
+// The launcher sizes the grid either to one tile per wave or to a fixed number
+// of resident workgroups.
+
+template <class T>
+__device__ __forceinline__ int64_t first_wave() {
+    return static_cast<int64_t>(blockIdx.x) * (kBlock / 64) + (threadIdx.x >> 6);
+}
+
+__device__ __forceinline__ int64_t wave_stride() {
+    return static_cast<int64_t>(gridDim.x) * (kBlock / 64);
+}
 
 // y may alias x: a lane reads all of its chunks before the row statistics
 // exist, and writes only the chunks it read.
-template <int C, int K>
-__global__ __launch_bounds__(kBlock) void ln_fixed_kernel(const uint4* x, uint4* y,
+template <int C, int K, class H>
+__global__ __launch_bounds__(kBlock) void ln_fixed_kernel(const chunk_t* x, chunk_t* y,
                                                           int64_t rows, double eps) {
     using T = Tile<C, K>;
-    int sub;
-    const int64_t row = tile_row<C, K>(sub);
-    const bool live = row < rows;
-    const int64_t base = row * T::kChunks + sub;
-    uint4 v[K];
-    zero(v);
-    if (live) {
+    const int lane = threadIdx.x & 63;
+    const int sub = lane % T::kLanes;
+    for (int64_t w = first_wave<T>(); w * T::kRowsPerWave < rows; w += wave_stride()) {
+        const int64_t row = w * T::kRowsPerWave + lane / T::kLanes;
+        const bool live = row < rows;
+        const int64_t base = row * T::kChunks + sub;
+        chunk_t v[K];
+        zero(v);
+        if (live) {
 #pragma unroll
-        for (int k = 0; k < K; ++k) v[k] = x[base + k * T::kLanes];
-    }
-    layer_norm_lane<C, K>(v, eps);
-    if (live) {
+            for (int k = 0; k < K; ++k) v[k] = load16<H>(x + base + k * T::kLanes);
+        }
+        layer_norm_lane<C, K>(v, eps);
+        if (live) {
 #pragma unroll
-        for (int k = 0; k < K; ++k) y[base + k * T::kLanes] = v[k];
+            for (int k = 0; k < K; ++k) store16<H>(y + base + k * T::kLanes, v[k]);
+        }
     }
 }
 
-template <int C, int K>
-__global__ __launch_bounds__(kBlock) void add_ln_kernel(const uint4* branch, const uint4* residual,
-                                                        uint4* residual_out, uint4* y,
+template <int C, int K, class H>
+__global__ __launch_bounds__(kBlock) void add_ln_kernel(const chunk_t* branch, const chunk_t* residual,
+                                                        chunk_t* residual_out, chunk_t* y,
                                                         int64_t rows, double eps) {
     using T = Tile<C, K>;
-    int sub;
-    const int64_t row = tile_row<C, K>(sub);
-    const bool live = row < rows;
-    const int64_t base = row * T::kChunks + sub;
-    uint4 b[K], r[K];
-    zero(b);
-    zero(r);
-    if (live) {
+    const int lane = threadIdx.x & 63;
+    const int sub = lane % T::kLanes;
+    for (int64_t w = first_wave<T>(); w * T::kRowsPerWave < rows; w += wave_stride()) {
+        const int64_t row = w * T::kRowsPerWave + lane / T::kLanes;
+        const bool live = row < rows;
+        const int64_t base = row * T::kChunks + sub;
+        chunk_t b[K], r[K];
+        zero(b);
+        zero(r);
+        if (live) {
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
-            b[k] = branch[base + k * T::kLanes];
-            r[k] = residual[base + k * T::kLanes];
+            for (int k = 0; k < K; ++k) {
+                b[k] = load16<H>(branch + base + k * T::kLanes);
+                r[k] = load16<H>(residual + base + k * T::kLanes);
+            }
         }
-    }
-    residual_add<K>(b, r);
-    if (live) {
+        residual_add<K>(b, r);
+        if (live) {
 #pragma unroll
-        for (int k = 0; k < K; ++k) residual_out[base + k * T::kLanes] = r[k];
-    }
-    layer_norm_lane<C, K>(r, eps);
-    if (live) {
+            for (int k = 0; k < K; ++k) store16<H>(residual_out + base + k * T::kLanes, r[k]);
+        }
+        layer_norm_lane<C, K>(r, eps);
+        if (live) {
 #pragma unroll
-        for (int k = 0; k < K; ++k) y[base + k * T::kLanes] = r[k];
+            for (int k = 0; k < K; ++k) store16<H>(y + base + k * T::kLanes, r[k]);
+        }
     }
 }
 
 // Output-major gather: lane group j reads table[j] and, for a valid entry,
 // the whole source row; padding and out-of-range entries read nothing and
 // store +0.0 (LayerNorm of a zero row is exactly +0.0 as well).
-template <int C, int K, bool kNorm>
-__global__ __launch_bounds__(kBlock) void gather_kernel(const uint4* __restrict__ x, int64_t n_src,
+template <int C, int K, bool kNorm, class H>
+__global__ __launch_bounds__(kBlock) void gather_kernel(const chunk_t* __restrict__ x, int64_t n_src,
                                                         const int32_t* __restrict__ table,
-                                                        int64_t n_out, uint4* __restrict__ out,
+                                                        int64_t n_out, chunk_t* __restrict__ out,
                                                         double eps) {
     using T = Tile<C, K>;
-    int sub;
-    const int64_t j = tile_row<C, K>(sub);
-    const bool live = j < n_out;
-    const int32_t t = live ? table[j] : -1;
-    const bool valid = t >= 0 && static_cast<int64_t>(t) < n_src;
-    const int64_t src = static_cast<int64_t>(t) * T::kChunks + sub;
-    uint4 v[K];
-    zero(v);
-    if (valid) {
+    const int lane = threadIdx.x & 63;
+    const int sub = lane % T::kLanes;
+    for (int64_t w = first_wave<T>(); w * T::kRowsPerWave < n_out; w += wave_stride()) {
+        const int64_t j = w * T::kRowsPerWave + lane / T::kLanes;
+        const bool live = j < n_out;
+        const int32_t t = live ? table[j] : -1;
+        const bool valid = t >= 0 && static_cast<int64_t>(t) < n_src;
+        const int64_t src = static_cast<int64_t>(t) * T::kChunks + sub;
+        chunk_t v[K];
+        zero(v);
+        if (valid) {
 #pragma unroll
-        for (int k = 0; k < K; ++k) v[k] = x[src + k * T::kLanes];
-    }
-    if constexpr (kNorm) layer_norm_lane<C, K>(v, eps);
-    if (live) {
-        const int64_t dst = j * T::kChunks + sub;
+            for (int k = 0; k < K; ++k) v[k] = load16<H>(x + src + k * T::kLanes);
+        }
+        if constexpr (kNorm) layer_norm_lane<C, K>(v, eps);
+        if (live) {
+            const int64_t dst = j * T::kChunks + sub;
 #pragma unroll
-        for (int k = 0; k < K; ++k) out[dst + k * T::kLanes] = v[k];
+            for (int k = 0; k < K; ++k) store16<H>(out + dst + k * T::kLanes, v[k]);
+        }
     }
 }
 
@@ -310,39 +342,82 @@ __global__ __launch_bounds__(kBlock) void window_index_kernel(WindowGeometry g, 
 }
 
 // ---------------------------------------------------------------------------
-// Launch helpers
+// Launch configuration
 
-template <int C>
+// Launch configuration, measured on MI355X with rotating (cache-cold) buffers.
+//
+// K (chunks per lane) is fixed per width, so that every LayerNorm kernel of one
+// width reduces a row in the same order and their outputs agree bit for bit:
+// K = 3 at C = 192 (8 lanes per row), K = 6 at C = 384 (8 lanes per row).
+// Memory hints and the grid are chosen per operation: 0 blocks per CU means one
+// tile per wave (a one-shot grid), otherwise the grid is capped at that many
+// workgroups per compute unit and each wave loops over tiles. Non-temporal
+// stores are always on (outputs are not re-read by the same kernel);
+// non-temporal loads pay off for the kernels that stream their inputs once.
+enum class Op { kLn, kAddLn, kGather, kNormGather };
+
+template <int C> struct Width;
+template <> struct Width<192> { static constexpr int K = 3; };
+template <> struct Width<384> { static constexpr int K = 6; };
+
+template <int C, Op O> struct Launch;
+template <> struct Launch<192, Op::kLn>         { using H = Hints<true, true>;  static constexpr int kBlocksPerCu = 0; };
+template <> struct Launch<192, Op::kAddLn>      { using H = Hints<true, true>;  static constexpr int kBlocksPerCu = 0; };
+template <> struct Launch<192, Op::kGather>     { using H = Hints<false, true>; static constexpr int kBlocksPerCu = 8; };
+template <> struct Launch<192, Op::kNormGather> { using H = Hints<true, true>;  static constexpr int kBlocksPerCu = 0; };
+template <> struct Launch<384, Op::kLn>         { using H = Hints<false, true>; static constexpr int kBlocksPerCu = 0; };
+template <> struct Launch<384, Op::kAddLn>      { using H = Hints<true, true>;  static constexpr int kBlocksPerCu = 0; };
+template <> struct Launch<384, Op::kGather>     { using H = Hints<false, true>; static constexpr int kBlocksPerCu = 0; };
+template <> struct Launch<384, Op::kNormGather> { using H = Hints<false, true>; static constexpr int kBlocksPerCu = 4; };
+
+int g_cus = 0;  // compute units of the current device, read once
+
+template <int C, Op O>
 unsigned grid_for(int64_t rows) {
-    using T = Tile<C, Config<C>::K>;
+    using T = Tile<C, Width<C>::K>;
     const int64_t tiles = (rows + T::kRowsPerWave - 1) / T::kRowsPerWave;
-    return static_cast<unsigned>((tiles + (kBlock / 64) - 1) / (kBlock / 64));
+    int64_t blocks = (tiles + (kBlock / 64) - 1) / (kBlock / 64);
+    if (Launch<C, O>::kBlocksPerCu > 0) {
+        if (g_cus == 0) {
+            int dev = 0, cus = 0;
+            if (hipGetDevice(&dev) == hipSuccess &&
+                hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+                cus > 0)
+                g_cus = cus;
+            else
+                g_cus = 256;
+        }
+        const int64_t cap = static_cast<int64_t>(g_cus) * Launch<C, O>::kBlocksPerCu;
+        if (blocks > cap) blocks = cap;
+    }
+    return static_cast<unsigned>(blocks);
 }
 
 template <int C>
 hipError_t ln_fixed_c(const void* x, void* y, int64_t rows, double eps, hipStream_t s) {
-    constexpr int K = Config<C>::K;
-    ln_fixed_kernel<C, K><<<grid_for<C>(rows), kBlock, 0, s>>>(
-        static_cast<const uint4*>(x), static_cast<uint4*>(y), rows, eps);
+    using L = Launch<C, Op::kLn>;
+    ln_fixed_kernel<C, Width<C>::K, typename L::H><<<grid_for<C, Op::kLn>(rows), kBlock, 0, s>>>(
+        static_cast<const chunk_t*>(x), static_cast<chunk_t*>(y), rows, eps);
     return hipGetLastError();
 }
 
 template <int C>
 hipError_t add_ln_c(const void* b, const void* r, void* ro, void* y, int64_t rows, double eps,
                     hipStream_t s) {
-    constexpr int K = Config<C>::K;
-    add_ln_kernel<C, K><<<grid_for<C>(rows), kBlock, 0, s>>>(
-        static_cast<const uint4*>(b), static_cast<const uint4*>(r), static_cast<uint4*>(ro),
-        static_cast<uint4*>(y), rows, eps);
+    using L = Launch<C, Op::kAddLn>;
+    add_ln_kernel<C, Width<C>::K, typename L::H><<<grid_for<C, Op::kAddLn>(rows), kBlock, 0, s>>>(
+        static_cast<const chunk_t*>(b), static_cast<const chunk_t*>(r), static_cast<chunk_t*>(ro),
+        static_cast<chunk_t*>(y), rows, eps);
     return hipGetLastError();
 }
 
 template <int C, bool kNorm>
 hipError_t gather_c(const void* x, int64_t n_src, const int32_t* table, int64_t n_out, double eps,
                     void* out, hipStream_t s) {
-    constexpr int K = Config<C>::K;
-    gather_kernel<C, K, kNorm><<<grid_for<C>(n_out), kBlock, 0, s>>>(
-        static_cast<const uint4*>(x), n_src, table, n_out, static_cast<uint4*>(out), eps);
+    constexpr Op O = kNorm ? Op::kNormGather : Op::kGather;
+    using L = Launch<C, O>;
+    gather_kernel<C, Width<C>::K, kNorm, typename L::H><<<grid_for<C, O>(n_out), kBlock, 0, s>>>(
+        static_cast<const chunk_t*>(x), n_src, table, n_out, static_cast<chunk_t*>(out), eps);
     return hipGetLastError();
 }
 
