@@ -87,6 +87,7 @@ class LevelBuffers:
         }
 
 
+SPIN_CYCLES = 5_000_000    # a few ms of GPU spin ahead of each per-kernel timed run
 COLD_BYTES = 5 << 28   # 1.25 GiB: reuse distance of any buffer in a timed run (MALL is 256 MB)
 
 
@@ -199,8 +200,8 @@ def main(argv=None):
     ap.add_argument("--kernel-reps", type=int, default=40, help="back-to-back launches per timed run")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="minimum oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=OPS, default=None,
-                    help="launch only this op, --steps times per level (for profiling runs)")
+    ap.add_argument("--only", choices=OPS + ("all",), default=None,
+                    help="launch only this op (or every op), --steps times per level (profiling runs)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="also run an elementwise copy of this many MiB (PMC calibration)")
     args = ap.parse_args(argv)
@@ -244,9 +245,11 @@ def main(argv=None):
     stream = torch.cuda.current_stream(dev)
 
     if args.only:
+        only = OPS if args.only == "all" else (args.only,)
         for lv in levels:
-            for i in range(args.warmup + args.steps):
-                sets[i % args.sets][lv.name].calls[args.only]()
+            for op in only:
+                for i in range(args.warmup + args.steps):
+                    sets[i % args.sets][lv.name].calls[op]()
         torch.cuda.synchronize()
         if args.calibration_copy_mib:
             n = args.calibration_copy_mib * (1 << 20) // 2
@@ -265,10 +268,14 @@ def main(argv=None):
             for op in OPS:
                 calls[op]()
 
-    def run_timed(launch, count):
+    def run_timed(launch, count, spin=True):
         """HIP events on the launch stream around `count` back-to-back launches;
-        returns the average microseconds per launch."""
+        returns the average microseconds per launch. A spin kernel queued first
+        keeps the GPU busy while the launches are enqueued, so host launch
+        latency never leaves the GPU idle inside the timed region."""
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        if spin:
+            torch.cuda._sleep(SPIN_CYCLES)
         a.record(stream)
         for i in range(count):
             launch(i)
@@ -281,8 +288,10 @@ def main(argv=None):
     torch.cuda.synchronize()
 
     # timed region 1: whole steps, wall clock (the value) and device time
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    step_dev_us = run_timed(step, args.steps)
+    step_dev_us = run_timed(step, args.steps, spin=False)
+    torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
 

@@ -185,6 +185,11 @@ LWG_EXPORT int32_t lwg_window_index_build(int32_t Z, int32_t H, int32_t W, int32
     g.nbh = g.Hp / wh; g.nbw = g.Wp / ww;
     g.win_tokens = wz * wh * ww;
     g.rows = static_cast<int32_t>(m);
+    g.div_win = lwg::make_fastdiv(static_cast<uint32_t>(g.win_tokens));
+    g.div_nbw = lwg::make_fastdiv(static_cast<uint32_t>(g.nbw));
+    g.div_nbh = lwg::make_fastdiv(static_cast<uint32_t>(g.nbh));
+    g.div_ww = lwg::make_fastdiv(static_cast<uint32_t>(ww));
+    g.div_wh = lwg::make_fastdiv(static_cast<uint32_t>(wh));
     return hip_result(lwg::launch_window_index(g, table, static_cast<hipStream_t>(stream)), fn);
 }
 

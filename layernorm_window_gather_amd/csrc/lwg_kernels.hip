@@ -312,23 +312,28 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(const chunk_t* __restric
     }
 }
 
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
+    return static_cast<uint32_t>((static_cast<uint64_t>(n) * f.m) >> f.s);
+}
+
 // One thread per table entry. Entry j = window * win_tokens + t; windows are
 // row-major over (bz, bh, bw), tokens row-major over (dz, dh, dw). Gathered
 // position p = (b*w + d) reads padded position (p + s) mod padded extent; a
-// position past the real grid on any axis is padding (-1).
+// position past the real grid on any axis is padding (-1). The divisions by
+// the window geometry use host-computed multiply-shift reciprocals.
 __global__ __launch_bounds__(kBlock) void window_index_kernel(WindowGeometry g, int32_t* table) {
-    const int32_t j = static_cast<int32_t>(blockIdx.x) * kBlock + static_cast<int32_t>(threadIdx.x);
-    if (j >= g.rows) return;
-    const int32_t wid = j / g.win_tokens;
-    const int32_t t = j - wid * g.win_tokens;
-    const int32_t bw = wid % g.nbw;
-    const int32_t bzh = wid / g.nbw;
-    const int32_t bh = bzh % g.nbh;
-    const int32_t bz = bzh / g.nbh;
-    const int32_t dw = t % g.ww;
-    const int32_t dzh = t / g.ww;
-    const int32_t dh = dzh % g.wh;
-    const int32_t dz = dzh / g.wh;
+    const uint32_t j = blockIdx.x * kBlock + threadIdx.x;
+    if (j >= static_cast<uint32_t>(g.rows)) return;
+    const uint32_t wid = fdiv(j, g.div_win);
+    const uint32_t t = j - wid * g.win_tokens;
+    const uint32_t bzh = fdiv(wid, g.div_nbw);
+    const uint32_t bw = wid - bzh * g.nbw;
+    const uint32_t bz = fdiv(bzh, g.div_nbh);
+    const uint32_t bh = bzh - bz * g.nbh;
+    const uint32_t dzh = fdiv(t, g.div_ww);
+    const uint32_t dw = t - dzh * g.ww;
+    const uint32_t dz = fdiv(dzh, g.div_wh);
+    const uint32_t dh = dzh - dz * g.wh;
     // b*w + d < padded extent and s < padded extent: the sum stays below 2^32
     int64_t qz = static_cast<int64_t>(bz) * g.wz + dz + g.sz;
     int64_t qh = static_cast<int64_t>(bh) * g.wh + dh + g.sh;
@@ -344,31 +349,30 @@ __global__ __launch_bounds__(kBlock) void window_index_kernel(WindowGeometry g, 
 // ---------------------------------------------------------------------------
 // Launch configuration
 
-// Launch configuration, measured on MI355X with rotating (cache-cold) buffers.
+// Launch configuration, measured on MI355X with cache-cold buffers (every
+// input re-read only after > 1 GiB of other traffic, so nothing is served from
+// the 256 MB Infinity Cache).
 //
 // K (chunks per lane) is fixed per width, so that every LayerNorm kernel of one
 // width reduces a row in the same order and their outputs agree bit for bit:
-// K = 3 at C = 192 (8 lanes per row), K = 6 at C = 384 (8 lanes per row).
-// Memory hints and the grid are chosen per operation: 0 blocks per CU means one
-// tile per wave (a one-shot grid), otherwise the grid is capped at that many
-// workgroups per compute unit and each wave loops over tiles. Non-temporal
-// stores are always on (outputs are not re-read by the same kernel);
-// non-temporal loads pay off for the kernels that stream their inputs once.
+// K = 3 at C = 192 and K = 6 at C = 384, i.e. 8 lanes per row, each wave
+// instruction reading whole 128-byte lines of 8 rows. (4 lanes per row, 64-byte
+// pieces of a line per instruction, measured 10-20% slower.)
+// Every kernel streams its inputs once and never re-reads its outputs, so all
+// loads and stores carry the non-temporal hint; on cold data that beat plain
+// and store-only-hinted accesses for every kernel. The grid is one tile per
+// wave, except the C = 384 norm-gather, which is capped at 4 workgroups per
+// compute unit with each wave looping over tiles.
 enum class Op { kLn, kAddLn, kGather, kNormGather };
 
 template <int C> struct Width;
 template <> struct Width<192> { static constexpr int K = 3; };
 template <> struct Width<384> { static constexpr int K = 6; };
 
-template <int C, Op O> struct Launch;
-template <> struct Launch<192, Op::kLn>         { using H = Hints<true, true>;  static constexpr int kBlocksPerCu = 0; };
-template <> struct Launch<192, Op::kAddLn>      { using H = Hints<true, true>;  static constexpr int kBlocksPerCu = 0; };
-template <> struct Launch<192, Op::kGather>     { using H = Hints<false, true>; static constexpr int kBlocksPerCu = 8; };
-template <> struct Launch<192, Op::kNormGather> { using H = Hints<true, true>;  static constexpr int kBlocksPerCu = 0; };
-template <> struct Launch<384, Op::kLn>         { using H = Hints<false, true>; static constexpr int kBlocksPerCu = 0; };
-template <> struct Launch<384, Op::kAddLn>      { using H = Hints<true, true>;  static constexpr int kBlocksPerCu = 0; };
-template <> struct Launch<384, Op::kGather>     { using H = Hints<false, true>; static constexpr int kBlocksPerCu = 0; };
-template <> struct Launch<384, Op::kNormGather> { using H = Hints<false, true>; static constexpr int kBlocksPerCu = 4; };
+using Streaming = Hints<true, true>;
+
+template <int C, Op O> struct Launch { using H = Streaming; static constexpr int kBlocksPerCu = 0; };
+template <> struct Launch<384, Op::kNormGather> { using H = Streaming; static constexpr int kBlocksPerCu = 4; };
 
 int g_cus = 0;  // compute units of the current device, read once
 

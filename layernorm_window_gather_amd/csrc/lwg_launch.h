@@ -9,6 +9,24 @@
 
 namespace lwg {
 
+// Division of a dividend below 2^31 by a fixed divisor d >= 1 with one 64-bit
+// multiply and a shift: q = (n * m) >> s with s = 31 + ceil(log2 d) and
+// m = ceil(2^s / d) < 2^32. The rounding error of m times n stays below 1/d for
+// every n < 2^31, so q is exactly floor(n / d) (the round-up reciprocal method
+// of Granlund and Montgomery, "Division by invariant integers using
+// multiplication", 1994).
+struct FastDiv {
+    uint32_t d, m, s;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+    uint32_t l = 0;
+    while ((uint64_t{1} << l) < d) ++l;
+    const uint32_t s = 31 + l;
+    const uint64_t num = uint64_t{1} << s;
+    return FastDiv{d, static_cast<uint32_t>((num + d - 1) / d), s};
+}
+
 // Geometry of one shifted-window table, reduced on the host: shifts already
 // taken modulo the padded extents, all products known to fit in int32.
 struct WindowGeometry {
@@ -19,6 +37,7 @@ struct WindowGeometry {
     int32_t nbh, nbw;       // windows along h and w
     int32_t win_tokens;     // wz * wh * ww
     int32_t rows;           // Zp * Hp * Wp
+    FastDiv div_win, div_nbw, div_nbh, div_ww, div_wh;
 };
 
 hipError_t launch_ln_fixed(const void* x, void* y, int64_t rows, int32_t C, double eps,
