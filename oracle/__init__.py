@@ -16,7 +16,12 @@ Everything is plain numpy in float64, written from the definitions on the page
   table per window shape, padding folded into the index protocol);
 * ``window_gather`` -- section 5 (index >= 0 copies the source token, -1 writes
   a zero row);
-* ``norm_gather`` -- section 5 (norm1's output feeds only the window gather).
+* ``norm_gather`` -- section 5 (norm1's output feeds only the window gather);
+* ``window_reverse`` / ``window_inverse_table`` -- the inverse of the window
+  partition (windows back to the grid, roll back, crop), which the pages imply
+  but do not describe;
+* ``window_reverse_add_ln`` / ``add_norm_gather`` -- the residual add + norm of
+  section 4 fused with the reverse, or with the forward gather of section 5.
 
 Each function is pinned by ``tests/test_oracle_pins.py`` to closed forms,
 brute force on tiny inputs, a library routine, or values derived by hand and
@@ -24,10 +29,12 @@ stored under ``tests/golden/``.
 """
 from .rowops import EPS, WIDTHS, fp16_round, residual_sum, layer_norm, add_ln
 from .window import (padded_extent, window_token_count, window_index_table,
-                     window_gather, norm_gather, norm_gather_rows)
+                     window_gather, norm_gather, norm_gather_rows, window_reverse,
+                     window_inverse_table, window_reverse_add_ln, add_norm_gather)
 
 __all__ = [
     "EPS", "WIDTHS", "fp16_round", "residual_sum", "layer_norm", "add_ln",
     "padded_extent", "window_token_count", "window_index_table", "window_gather",
-    "norm_gather", "norm_gather_rows",
+    "norm_gather", "norm_gather_rows", "window_reverse", "window_inverse_table",
+    "window_reverse_add_ln", "add_norm_gather",
 ]

@@ -84,3 +84,49 @@ def norm_gather_rows(x: np.ndarray, table: np.ndarray, rows: np.ndarray,
     if valid.any():
         out[valid] = layer_norm(x[t[valid]], eps)
     return out
+
+
+def window_reverse(rows: np.ndarray, grid, window, shift=(0, 0, 0)) -> np.ndarray:
+    """Undo the window partition: the gathered rows [M, C] (window-major) are put
+    back on the padded grid, rolled back by +shift, and the padding is cropped,
+    giving [Z*H*W, C] in token order. This is the step that follows attention in a
+    shifted-window block; the pages describe only the forward gather, so the
+    reverse is read as the forward steps undone in the opposite order."""
+    Z, H, W = grid
+    wz, wh, ww = window
+    Zp, Hp, Wp = (padded_extent(g, w) for g, w in zip(grid, window))
+    rows = np.asarray(rows)
+    c = rows.shape[1]
+    if rows.shape[0] != Zp * Hp * Wp:
+        raise ValueError("row count differs from the window token count")
+    g = rows.reshape(Zp // wz, Hp // wh, Wp // ww, wz, wh, ww, c)
+    g = g.transpose(0, 3, 1, 4, 2, 5, 6).reshape(Zp, Hp, Wp, c)
+    g = np.roll(g, shift=tuple(shift), axis=(0, 1, 2))
+    return np.ascontiguousarray(g[:Z, :H, :W].reshape(Z * H * W, c))
+
+
+def window_inverse_table(grid, window, shift=(0, 0, 0)) -> np.ndarray:
+    """INT32 table, one entry per source token: the gathered row that holds it.
+    Obtained by running window_reverse on the column of gathered-row numbers."""
+    m = window_token_count(grid, window)
+    ids = np.arange(m, dtype=np.int64)[:, None]
+    return window_reverse(ids, grid, window, shift)[:, 0].astype(np.int32)
+
+
+def window_reverse_add_ln(rows: np.ndarray, residual: np.ndarray, grid, window, shift=(0, 0, 0),
+                          eps: float = 1e-5):
+    """Window reverse of the attention output used as the branch of the residual
+    add + LayerNorm of section 4 of the BW1000 page: returns (FP16(residual +
+    reversed rows), LayerNorm of that)."""
+    from .rowops import add_ln
+    branch = window_reverse(np.asarray(rows, dtype=np.float16), grid, window, shift)
+    return add_ln(branch, residual, eps)
+
+
+def add_norm_gather(branch: np.ndarray, residual: np.ndarray, table: np.ndarray, eps: float = 1e-5):
+    """Residual add + LayerNorm + window gather: the FP16 residual sum of section 4
+    of the BW1000 page is written out, and its LayerNorm is only ever gathered
+    (section 5). Returns (residual_out, gathered rows)."""
+    from .rowops import residual_sum
+    r = residual_sum(residual, branch)
+    return r, norm_gather(r, table, eps)

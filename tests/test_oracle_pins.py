@@ -320,3 +320,78 @@ def test_norm_gather_rows_agrees_with_full_norm_gather():
     rows = np.array([0, 1, 100, 575, int(np.argmax(t == 3))])
     assert np.array_equal(bits_of(oracle.norm_gather_rows(x, t, rows)), bits_of(full[rows]))
     assert not bits_of(full[int(np.argmax(t == 3))]).any()
+
+
+# ---------------------------------------------------------------------------
+# window reverse and the fused rows built on it
+
+
+def brute_force_inverse(grid, window, shift):
+    """Loop form: for each token, find its rolled position, its window and the
+    offset inside the window."""
+    Z, H, W = grid
+    wz, wh, ww = window
+    Zp, Hp, Wp = (-(-Z // wz) * wz, -(-H // wh) * wh, -(-W // ww) * ww)
+    nbh, nbw = Hp // wh, Wp // ww
+    out = []
+    for z in range(Z):
+        for h in range(H):
+            for w in range(W):
+                gz, gh, gw = (z - shift[0]) % Zp, (h - shift[1]) % Hp, (w - shift[2]) % Wp
+                win = ((gz // wz) * nbh + gh // wh) * nbw + gw // ww
+                off = ((gz % wz) * wh + gh % wh) * ww + gw % ww
+                out.append(win * wz * wh * ww + off)
+    return np.array(out, dtype=np.int32)
+
+
+def test_window_inverse_golden_points(golden_dir):
+    spec = json.load(open(os.path.join(golden_dir, "window_inverse_points.json")))
+    for case in spec["cases"]:
+        inv = oracle.window_inverse_table(tuple(case["grid"]), tuple(case["window"]), tuple(case["shift"]))
+        for i, j in case["points"].items():
+            assert int(inv[int(i)]) == j, (case["grid"], case["shift"], i)
+
+
+@pytest.mark.parametrize("grid", [(2, 12, 24), (2, 7, 13), (4, 9, 26), (1, 1, 1), (5, 11, 25)])
+@pytest.mark.parametrize("shift", [(0, 0, 0), (1, 3, 6), (3, 13, 30)])
+def test_window_inverse_matches_brute_force_and_forward(grid, shift):
+    inv = oracle.window_inverse_table(grid, workloads.WINDOW, shift)
+    assert np.array_equal(inv, brute_force_inverse(grid, workloads.WINDOW, shift))
+    t = oracle.window_index_table(grid, workloads.WINDOW, shift)
+    assert np.array_equal(t[inv], np.arange(int(np.prod(grid)), dtype=np.int32))
+
+
+@pytest.mark.parametrize("grid", [(2, 12, 24), (4, 9, 26), (3, 13, 25)])
+@pytest.mark.parametrize("shift", [(0, 0, 0), (1, 3, 6)])
+def test_window_reverse_undoes_the_gather(grid, shift):
+    n = int(np.prod(grid))
+    x = workloads.normal_rows(71, n, 192)
+    t = oracle.window_index_table(grid, workloads.WINDOW, shift)
+    back = oracle.window_reverse(oracle.window_gather(x, t), grid, workloads.WINDOW, shift)
+    assert np.array_equal(bits_of(back), bits_of(x))
+
+
+def test_window_reverse_drops_padding_rows():
+    grid = (2, 7, 13)
+    t = oracle.window_index_table(grid, workloads.WINDOW, (1, 3, 6))
+    rows = np.where(t[:, None] >= 0, 1.0, 7.0).astype(np.float16).repeat(192, axis=1)
+    back = oracle.window_reverse(rows, grid, workloads.WINDOW, (1, 3, 6))
+    assert back.shape == (int(np.prod(grid)), 192) and (back == 1.0).all()
+
+
+def test_window_reverse_add_ln_and_add_norm_gather_compose():
+    grid = (2, 7, 13)
+    n = int(np.prod(grid))
+    t = oracle.window_index_table(grid, workloads.WINDOW, (1, 3, 6))
+    attn = workloads.normal_rows(72, t.size, 192)
+    res = workloads.normal_rows(73, n, 192)
+    r, y = oracle.window_reverse_add_ln(attn, res, grid, workloads.WINDOW, (1, 3, 6))
+    inv = oracle.window_inverse_table(grid, workloads.WINDOW, (1, 3, 6))
+    for i in (0, 5, n - 1):   # token i adds the attention row that holds it
+        exact = res[i].astype(np.float64) + attn[inv[i]].astype(np.float64)
+        assert np.array_equal(bits_of(r[i]), bits_of(exact.astype(np.float16)))
+    assert np.array_equal(bits_of(y), bits_of(oracle.layer_norm(r)))
+    br = workloads.normal_rows(74, n, 192)
+    r2, g = oracle.add_norm_gather(br, res, t)
+    assert np.array_equal(bits_of(r2), bits_of(oracle.residual_sum(res, br)))
+    assert np.array_equal(bits_of(g), bits_of(oracle.window_gather(oracle.layer_norm(r2), t)))
