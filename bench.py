@@ -52,10 +52,21 @@ def algorithmic_bytes(op: str, n: int, m: int, c: int) -> int:
         return INDEX * m
     if op in ("window_gather", "norm_gather"):
         return n * c * HALF + m * c * HALF + INDEX * m
+    if op == "window_inverse_build":
+        return INDEX * n
+    if op == "window_reverse_add_ln":
+        # reads the n window rows that hold tokens, the residual and the inverse
+        # table; writes residual_out and y
+        return 4 * n * c * HALF + INDEX * n
+    if op == "add_norm_gather":
+        # reads branch and residual, writes residual_out and the m gathered rows
+        return 3 * n * c * HALF + m * c * HALF + INDEX * m
     raise ValueError(op)
 
 
 OPS = ("ln_fixed", "add_ln", "window_index_build", "window_gather", "norm_gather")
+# the fused rows around the gather, reported per kernel (not part of the step)
+NEXT_OPS = ("window_inverse_build", "window_reverse_add_ln", "add_norm_gather")
 
 
 def level_inputs(level):
@@ -107,6 +118,18 @@ def op_pool(lwg, torch, dev, level, op, x_dev, res_dev, table, m, nbytes):
         elif op == "window_index_build":
             t = torch.empty(m, dtype=torch.int32, device=dev)
             calls.append(lwg.prepare(op, t, grid=level.grid, window=WINDOW, shift=SHIFT))
+        elif op == "window_inverse_build":
+            t = torch.empty(n, dtype=torch.int32, device=dev)
+            calls.append(lwg.prepare(op, t, grid=level.grid, window=WINDOW, shift=SHIFT))
+        elif op == "window_reverse_add_ln":
+            rows = lwg.window_gather(x_dev, table)            # window-ordered rows, padding = 0
+            inv = lwg.window_inverse_table(level.grid, WINDOW, SHIFT, device=dev)
+            r = res_dev.clone()
+            calls.append(lwg.prepare(op, rows, inv, r, torch.empty_like(r), torch.empty_like(r)))
+        elif op == "add_norm_gather":
+            b, r = x_dev.clone(), res_dev.clone()
+            calls.append(lwg.prepare(op, b, r, torch.empty_like(r), table,
+                                     torch.empty(m, c, dtype=torch.float16, device=dev)))
         else:
             x = x_dev.clone()
             calls.append(lwg.prepare(op, x, table, torch.empty(m, c, dtype=torch.float16, device=dev)))
@@ -240,8 +263,8 @@ def main(argv=None):
     parity_gate(lwg, torch, sets, host, levels, m_of)
 
     bytes_of = {(lv.name, op): algorithmic_bytes(op, lv.tokens, m_of[lv.name], lv.channels)
-                for lv in levels for op in OPS}
-    step_bytes = sum(bytes_of.values())
+                for lv in levels for op in OPS + NEXT_OPS}
+    step_bytes = sum(bytes_of[(lv.name, op)] for lv in levels for op in OPS)
     stream = torch.cuda.current_stream(dev)
 
     if args.only:
@@ -321,7 +344,7 @@ def main(argv=None):
     # 5 runs of kernel_reps launches
     kernels = {}
     for lv in levels:
-        for op in OPS:
+        for op in OPS + NEXT_OPS:
             pool = pool_for(lv, op)
             f = lambda i, pool=pool: pool[i % len(pool)]()  # noqa: E731
             for i in range(len(pool)):
@@ -332,8 +355,9 @@ def main(argv=None):
             med = float(np.median(runs))
             gbs = bytes_of[(lv.name, op)] / (med * 1e-6) / 1e9
             kernels[f"{op}@{lv.name}"] = {
-                "C": lv.channels, "rows_in": lv.tokens,
-                "rows_out": m_of[lv.name] if op in ("window_gather", "norm_gather", "window_index_build") else lv.tokens,
+                "C": lv.channels, "rows_in": lv.tokens, "in_step": op in OPS,
+                "rows_out": m_of[lv.name] if op in ("window_gather", "norm_gather", "window_index_build",
+                                                    "add_norm_gather") else lv.tokens,
                 "bytes": bytes_of[(lv.name, op)], "avg_us": round(med, 2),
                 "min_run_us": round(float(runs.min()), 2), "max_run_us": round(float(runs.max()), 2),
                 "GBps": round(gbs, 1), "pct_of_peak": round(100 * gbs / PEAK_GBS, 1),

@@ -125,6 +125,57 @@ int32_t lwg_window_gather(const void* x, int64_t n_src, int32_t C, const int32_t
 int32_t lwg_norm_gather(const void* x, int64_t n_src, int32_t C, const int32_t* table,
                         int64_t n_out, double eps, void* out, void* stream);
 
+/*
+ * Inverse window table: one INT32 entry per source token (Z*H*W of them), the
+ * gathered row that lwg_window_index_build's table sends that token to. Same
+ * geometry arguments and rules as lwg_window_index_build. It drives the window
+ * reverse that follows attention in a shifted-window block: the BW1000 page,
+ * section 5, describes the forward gather; the reverse undoes it (windows back
+ * onto the padded grid, roll back by +shift, crop the padding).
+ * inverse     : device int32 [inverse_len], written by one kernel on `stream`.
+ * inverse_len : must equal Z*H*W, else LWG_ERR_SIZE_MISMATCH.
+ * The plain window reverse is lwg_window_gather(window_rows, M, C, inverse, Z*H*W, out).
+ */
+int32_t lwg_window_inverse_build(int32_t Z, int32_t H, int32_t W,
+                                 int32_t wz, int32_t wh, int32_t ww,
+                                 int32_t sz, int32_t sh, int32_t sw,
+                                 int32_t* inverse, int64_t inverse_len, void* stream);
+
+/*
+ * Window reverse fused with residual add + LayerNorm (BW1000 page, section 4,
+ * applied to the attention output that comes back in window order):
+ *   branch[i]       = win[inverse[i]] if 0 <= inverse[i] < n_win, else +0.0
+ *   residual_out[i] = FP16(residual[i] + branch[i])
+ *   y[i]            = LayerNorm(residual_out[i])
+ * win             : [n_win, C] binary16 rows in window order (padding rows are
+ *                   never read).
+ * inverse         : device int32 [rows], 4-byte aligned (lwg_window_inverse_build).
+ * residual, residual_out, y : [rows, C] binary16. residual_out and y may each
+ *                   equal residual; y and residual_out must not overlap; no output
+ *                   may overlap win or inverse (LWG_ERR_ALIASING).
+ * rows and n_win must not exceed INT32_MAX.
+ */
+int32_t lwg_window_reverse_add_ln(const void* win, int64_t n_win, const int32_t* inverse,
+                                  const void* residual, void* residual_out, void* y,
+                                  int64_t rows, int32_t C, double eps, void* stream);
+
+/*
+ * Residual add + LayerNorm + window gather (BW1000 page, sections 4 and 5: the
+ * residual sum is rounded to FP16 once and written; its LayerNorm feeds only the
+ * window gather, so the normalised tensor is never written):
+ *   residual_out[t] = FP16(residual[t] + branch[t])            for every token t
+ *   out[j]          = LayerNorm(residual_out[table[j]])  if 0 <= table[j] < n_src,
+ *                     else +0.0
+ * branch, residual, residual_out : [n_src, C] binary16; out : [n_out, C].
+ * The valid entries of table must be distinct and cover every token (the tables
+ * of lwg_window_index_build are); a token no entry names keeps its residual_out
+ * row unwritten. residual_out may equal residual or branch. out must not
+ * overlap any other argument, and residual_out must not overlap table.
+ */
+int32_t lwg_add_norm_gather(const void* branch, const void* residual, void* residual_out,
+                            int64_t n_src, int32_t C, const int32_t* table, int64_t n_out,
+                            double eps, void* out, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* lwg_status_string(int32_t status);
 

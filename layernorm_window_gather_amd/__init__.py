@@ -16,6 +16,13 @@ Operations (page "Pangu-Weather inference optimisation on Hygon BW1000
   window_table(grid, window, shift)  the same, cached per key and device
   window_gather(x, table)            out[j] = x[table[j]], or zeros for -1
   norm_gather(x, table)              out[j] = LayerNorm(x[table[j]]), or zeros
+
+and the window reverse that follows attention, plus the two fusions around it:
+  window_inverse_build(grid, window, shift)  token -> gathered row, on the device
+  window_inverse_table(grid, window, shift)  the same, cached
+  window_reverse(rows, inverse)      rows back to token order (a gather by inverse)
+  window_reverse_add_ln(rows, inverse, residual)  reverse + add + LayerNorm
+  add_norm_gather(branch, residual, table)        add + LayerNorm + gather
 """
 from __future__ import annotations
 
@@ -27,7 +34,9 @@ from . import _lib
 from ._lib import LwgError
 
 __all__ = ["ln_fixed", "add_ln", "window_token_count", "window_index_build", "window_table",
-           "window_gather", "norm_gather", "LwgError", "WIDTHS", "EPS", "library"]
+           "window_gather", "norm_gather", "window_inverse_build", "window_inverse_table",
+           "window_reverse", "window_reverse_add_ln", "add_norm_gather", "LwgError", "WIDTHS", "EPS",
+           "library"]
 
 WIDTHS = (192, 384)
 EPS = 1e-5
@@ -197,6 +206,96 @@ def norm_gather(x: torch.Tensor, table: torch.Tensor, eps: float = EPS,
     return o
 
 
+def _token_count(grid) -> int:
+    g = _triple(grid, "grid")
+    if min(g) < 0:
+        raise RuntimeError(f"invalid grid {g}")
+    return g[0] * g[1] * g[2]
+
+
+def window_inverse_build(grid, window, shift=(0, 0, 0), device=None, out: torch.Tensor = None) -> torch.Tensor:
+    """Build the INT32 inverse table (token -> gathered row) on the device."""
+    g, w, s = _triple(grid, "grid"), _triple(window, "window"), _triple(shift, "shift")
+    n = _token_count(g)
+    if out is None:
+        dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+        if dev.type != "cuda":
+            raise RuntimeError(f"window tables live on a GPU device, got {dev}")
+        out = torch.empty(n, dtype=torch.int32, device=dev)
+    elif out.dtype != torch.int32 or out.device.type != "cuda" or not out.is_contiguous() or out.dim() != 1:
+        raise RuntimeError("out must be a contiguous 1-D int32 GPU tensor")
+    lib = _lib.load()
+    with torch.cuda.device(out.device):
+        _lib.check(lib.lwg_window_inverse_build(*g, *w, *s, ctypes.c_void_p(out.data_ptr()), out.numel(),
+                                                _stream(out.device)))
+    return out
+
+
+_inverses = {}
+
+
+def window_inverse_table(grid, window, shift=(0, 0, 0), device=None) -> torch.Tensor:
+    """Cached ``window_inverse_build``: one table per (grid, window, shift, device)."""
+    g, w, s = _triple(grid, "grid"), _triple(window, "window"), _triple(shift, "shift")
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    if dev.index is None:
+        dev = torch.device("cuda", torch.cuda.current_device())
+    key = (g, w, s, dev.index)
+    t = _inverses.get(key)
+    if t is None:
+        t = window_inverse_build(g, w, s, device=dev)
+        _inverses[key] = t
+    return t
+
+
+def window_reverse(rows: torch.Tensor, inverse: torch.Tensor, out: torch.Tensor = None) -> torch.Tensor:
+    """Window-ordered rows back to token order: out[i] = rows[inverse[i]]. This is
+    the window gather driven by the inverse table (the same kernel)."""
+    return window_gather(rows, inverse, out=out)
+
+
+def window_reverse_add_ln(rows: torch.Tensor, inverse: torch.Tensor, residual: torch.Tensor,
+                          eps: float = EPS, residual_out: torch.Tensor = None, out: torch.Tensor = None):
+    """Returns (FP16(residual + rows[inverse]), LayerNorm of it): the window reverse
+    of an attention output fused with the residual add + LayerNorm."""
+    n_win = _rows(rows, "rows")
+    n = _rows(residual, "residual")
+    if rows.shape[-1] != residual.shape[-1]:
+        raise RuntimeError("rows and residual widths differ")
+    if not isinstance(inverse, torch.Tensor) or inverse.dtype != torch.int32 or inverse.dim() != 1 \
+            or not inverse.is_contiguous() or inverse.numel() != n:
+        raise RuntimeError("inverse must be a contiguous 1-D int32 tensor with one entry per residual row")
+    _same_device(residual, ("rows", rows), ("inverse", inverse))
+    r = _out_like(residual_out, residual.shape, residual.device, "residual_out")
+    y = _out_like(out, residual.shape, residual.device, "out")
+    lib = _lib.load()
+    with torch.cuda.device(residual.device):
+        _lib.check(lib.lwg_window_reverse_add_ln(_ptr(rows), n_win, _ptr(inverse), _ptr(residual), _ptr(r),
+                                                 _ptr(y), n, residual.shape[-1], float(eps),
+                                                 _stream(residual.device)))
+    return r, y
+
+
+def add_norm_gather(branch: torch.Tensor, residual: torch.Tensor, table: torch.Tensor, eps: float = EPS,
+                    residual_out: torch.Tensor = None, out: torch.Tensor = None):
+    """Returns (FP16(residual + branch), gathered LayerNorm of it): out[j] is the
+    LayerNorm of residual_out[table[j]], or zeros for padding. The table's valid
+    entries must be distinct and cover every token (window_index_build's are)."""
+    n_src, shape = _gather_args(residual, table, "add_norm_gather")
+    _rows(branch, "branch")
+    if tuple(branch.shape) != tuple(residual.shape):
+        raise RuntimeError(f"branch shape {tuple(branch.shape)} != residual shape {tuple(residual.shape)}")
+    _same_device(residual, ("branch", branch))
+    r = _out_like(residual_out, residual.shape, residual.device, "residual_out")
+    o = _out_like(out, shape, residual.device, "out")
+    lib = _lib.load()
+    with torch.cuda.device(residual.device):
+        _lib.check(lib.lwg_add_norm_gather(_ptr(branch), _ptr(residual), _ptr(r), n_src, residual.shape[-1],
+                                           _ptr(table), table.numel(), float(eps), _ptr(o),
+                                           _stream(residual.device)))
+    return r, o
+
+
 class Prepared:
     """A checked, pre-marshalled call of one C entry point on fixed tensors and a
     fixed stream (the device's current stream when prepared). Calling it only
@@ -217,7 +316,10 @@ def prepare(op: str, *tensors, eps: float = EPS, grid=None, window=None, shift=(
       prepare("add_ln", branch, residual, residual_out, y)
       prepare("window_index_build", table, grid=..., window=..., shift=...)
       prepare("window_gather", x, table, out)
-      prepare("norm_gather", x, table, out)"""
+      prepare("norm_gather", x, table, out)
+      prepare("window_inverse_build", inverse, grid=..., window=..., shift=...)
+      prepare("window_reverse_add_ln", rows, inverse, residual, residual_out, y)
+      prepare("add_norm_gather", branch, residual, residual_out, table, out)"""
     lib = _lib.load()
     if op == "ln_fixed":
         x, y = tensors
@@ -254,6 +356,32 @@ def prepare(op: str, *tensors, eps: float = EPS, grid=None, window=None, shift=(
         else:
             fn, args = lib.lwg_norm_gather, (_ptr(x), n_src, x.shape[-1], _ptr(table), table.numel(),
                                              float(eps), _ptr(out), _stream(dev))
+    elif op == "window_inverse_build":
+        (inv,) = tensors
+        g, w, s = _triple(grid, "grid"), _triple(window, "window"), _triple(shift, "shift")
+        if inv.dtype != torch.int32 or inv.device.type != "cuda" or not inv.is_contiguous():
+            raise RuntimeError("inverse must be a contiguous int32 GPU tensor")
+        dev = inv.device
+        fn, args = lib.lwg_window_inverse_build, (*g, *w, *s, _ptr(inv), inv.numel(), _stream(dev))
+    elif op == "window_reverse_add_ln":
+        rows, inv, r, ro, y = tensors
+        n_win, n = _rows(rows, "rows"), _rows(r, "residual")
+        _out_like(ro, r.shape, r.device, "residual_out")
+        _out_like(y, r.shape, r.device, "y")
+        if inv.dtype != torch.int32 or inv.numel() != n or not inv.is_contiguous():
+            raise RuntimeError("inverse must be a contiguous int32 tensor with one entry per residual row")
+        dev = r.device
+        fn, args = lib.lwg_window_reverse_add_ln, (_ptr(rows), n_win, _ptr(inv), _ptr(r), _ptr(ro), _ptr(y), n,
+                                                   r.shape[-1], float(eps), _stream(dev))
+    elif op == "add_norm_gather":
+        b, r, ro, table, out = tensors
+        n_src, shape = _gather_args(r, table, op)
+        _rows(b, "branch")
+        _out_like(ro, r.shape, r.device, "residual_out")
+        _out_like(out, shape, r.device, "out")
+        dev = r.device
+        fn, args = lib.lwg_add_norm_gather, (_ptr(b), _ptr(r), _ptr(ro), n_src, r.shape[-1], _ptr(table),
+                                             table.numel(), float(eps), _ptr(out), _stream(dev))
     else:
         raise ValueError(f"unknown op {op!r}")
     return Prepared(fn, args, tensors)

@@ -152,10 +152,13 @@ LWG_EXPORT int64_t lwg_window_token_count(int32_t Z, int32_t H, int32_t W, int32
     return n > INT32_MAX ? -1 : n;
 }
 
-LWG_EXPORT int32_t lwg_window_index_build(int32_t Z, int32_t H, int32_t W, int32_t wz, int32_t wh,
-                                          int32_t ww, int32_t sz, int32_t sh, int32_t sw,
-                                          int32_t* table, int64_t table_len, void* stream) {
-    static const char* fn = "lwg_window_index_build";
+namespace {
+
+// Checks the window geometry shared by both table builders and fills g; `len`
+// must equal `expect` (the table length the geometry implies).
+int32_t window_geometry(const char* fn, int32_t Z, int32_t H, int32_t W, int32_t wz, int32_t wh,
+                        int32_t ww, int32_t sz, int32_t sh, int32_t sw, lwg::WindowGeometry& g,
+                        int64_t* rows_out, int64_t* tokens_out) {
     if (Z < 0 || H < 0 || W < 0)
         return fail(LWG_ERR_INVALID_ARGUMENT, "%s: grid extents must be >= 0 (got %d,%d,%d)", fn, Z, H, W);
     if (wz < 1 || wh < 1 || ww < 1)
@@ -168,14 +171,9 @@ LWG_EXPORT int32_t lwg_window_index_build(int32_t Z, int32_t H, int32_t W, int32
     const int64_t m = lwg_window_token_count(Z, H, W, wz, wh, ww);
     if (m < 0)
         return fail(LWG_ERR_INVALID_ARGUMENT, "%s: padded grid holds more than 2^31-1 rows", fn);
-    if (table_len != m)
-        return fail(LWG_ERR_SIZE_MISMATCH, "%s: table_len=%lld but the window token count is %lld", fn,
-                    static_cast<long long>(table_len), static_cast<long long>(m));
-    if (m == 0) return ok();
-    if (table == nullptr) return fail(LWG_ERR_INVALID_ARGUMENT, "%s: table is NULL", fn);
-    if ((reinterpret_cast<uintptr_t>(table) & 3u) != 0)
-        return fail(LWG_ERR_MISALIGNED, "%s: table is not 4-byte aligned", fn);
-    lwg::WindowGeometry g;
+    *rows_out = m;
+    *tokens_out = tokens;
+    if (m == 0) return LWG_OK;
     g.Z = Z; g.H = H; g.W = W;
     g.wz = wz; g.wh = wh; g.ww = ww;
     g.Zp = static_cast<int32_t>(padded(Z, wz));
@@ -190,7 +188,51 @@ LWG_EXPORT int32_t lwg_window_index_build(int32_t Z, int32_t H, int32_t W, int32
     g.div_nbh = lwg::make_fastdiv(static_cast<uint32_t>(g.nbh));
     g.div_ww = lwg::make_fastdiv(static_cast<uint32_t>(ww));
     g.div_wh = lwg::make_fastdiv(static_cast<uint32_t>(wh));
+    g.div_wz = lwg::make_fastdiv(static_cast<uint32_t>(wz));
+    g.div_W = lwg::make_fastdiv(static_cast<uint32_t>(W > 0 ? W : 1));
+    g.div_H = lwg::make_fastdiv(static_cast<uint32_t>(H > 0 ? H : 1));
+    return LWG_OK;
+}
+
+int32_t check_table_ptr(const char* fn, const char* name, const int32_t* t) {
+    if (t == nullptr) return fail(LWG_ERR_INVALID_ARGUMENT, "%s: %s is NULL", fn, name);
+    if ((reinterpret_cast<uintptr_t>(t) & 3u) != 0)
+        return fail(LWG_ERR_MISALIGNED, "%s: %s is not 4-byte aligned", fn, name);
+    return LWG_OK;
+}
+
+}  // namespace
+
+LWG_EXPORT int32_t lwg_window_index_build(int32_t Z, int32_t H, int32_t W, int32_t wz, int32_t wh,
+                                          int32_t ww, int32_t sz, int32_t sh, int32_t sw,
+                                          int32_t* table, int64_t table_len, void* stream) {
+    static const char* fn = "lwg_window_index_build";
+    lwg::WindowGeometry g;
+    int64_t m = 0, tokens = 0;
+    int32_t st = window_geometry(fn, Z, H, W, wz, wh, ww, sz, sh, sw, g, &m, &tokens);
+    if (st) return st;
+    if (table_len != m)
+        return fail(LWG_ERR_SIZE_MISMATCH, "%s: table_len=%lld but the window token count is %lld", fn,
+                    static_cast<long long>(table_len), static_cast<long long>(m));
+    if (m == 0) return ok();
+    if ((st = check_table_ptr(fn, "table", table))) return st;
     return hip_result(lwg::launch_window_index(g, table, static_cast<hipStream_t>(stream)), fn);
+}
+
+LWG_EXPORT int32_t lwg_window_inverse_build(int32_t Z, int32_t H, int32_t W, int32_t wz, int32_t wh,
+                                            int32_t ww, int32_t sz, int32_t sh, int32_t sw,
+                                            int32_t* inverse, int64_t inverse_len, void* stream) {
+    static const char* fn = "lwg_window_inverse_build";
+    lwg::WindowGeometry g;
+    int64_t m = 0, tokens = 0;
+    int32_t st = window_geometry(fn, Z, H, W, wz, wh, ww, sz, sh, sw, g, &m, &tokens);
+    if (st) return st;
+    if (inverse_len != tokens)
+        return fail(LWG_ERR_SIZE_MISMATCH, "%s: inverse_len=%lld but the grid holds %lld tokens", fn,
+                    static_cast<long long>(inverse_len), static_cast<long long>(tokens));
+    if (tokens == 0) return ok();
+    if ((st = check_table_ptr(fn, "inverse", inverse))) return st;
+    return hip_result(lwg::launch_window_inverse(g, inverse, static_cast<hipStream_t>(stream)), fn);
 }
 
 namespace {
@@ -237,5 +279,65 @@ LWG_EXPORT int32_t lwg_norm_gather(const void* x, int64_t n_src, int32_t C, cons
     if (n_out == 0) return ok();
     return hip_result(lwg::launch_norm_gather(x, n_src, C, table, n_out, eps, out,
                                               static_cast<hipStream_t>(stream)),
+                      fn);
+}
+
+LWG_EXPORT int32_t lwg_window_reverse_add_ln(const void* win, int64_t n_win, const int32_t* inverse,
+                                             const void* residual, void* residual_out, void* y,
+                                             int64_t rows, int32_t C, double eps, void* stream) {
+    static const char* fn = "lwg_window_reverse_add_ln";
+    int32_t st;
+    if ((st = check_width(fn, C)) || (st = check_eps(fn, eps)) || (st = check_rows(fn, "rows", rows)) ||
+        (st = check_rows(fn, "n_win", n_win)))
+        return st;
+    if (rows == 0) return ok();
+    if ((n_win > 0 && (st = check_tensor(fn, "win", win))) || (st = check_table_ptr(fn, "inverse", inverse)) ||
+        (st = check_tensor(fn, "residual", residual)) || (st = check_tensor(fn, "residual_out", residual_out)) ||
+        (st = check_tensor(fn, "y", y)))
+        return st;
+    const uint64_t bytes = static_cast<uint64_t>(rows) * C * 2;
+    const uint64_t win_bytes = static_cast<uint64_t>(n_win) * C * 2;
+    if (overlap(y, bytes, residual_out, bytes))
+        return fail(LWG_ERR_ALIASING, "%s: y and residual_out overlap", fn);
+    if (!same_or_disjoint(residual_out, residual, bytes) || !same_or_disjoint(y, residual, bytes))
+        return fail(LWG_ERR_ALIASING, "%s: an output partially overlaps residual", fn);
+    if ((n_win > 0 && (overlap(residual_out, bytes, win, win_bytes) || overlap(y, bytes, win, win_bytes))) ||
+        overlap(residual_out, bytes, inverse, static_cast<uint64_t>(rows) * 4) ||
+        overlap(y, bytes, inverse, static_cast<uint64_t>(rows) * 4))
+        return fail(LWG_ERR_ALIASING, "%s: an output overlaps win or inverse", fn);
+    return hip_result(lwg::launch_reverse_add_ln(win, n_win, inverse, residual, residual_out, y, rows, C, eps,
+                                                 static_cast<hipStream_t>(stream)),
+                      fn);
+}
+
+LWG_EXPORT int32_t lwg_add_norm_gather(const void* branch, const void* residual, void* residual_out,
+                                       int64_t n_src, int32_t C, const int32_t* table, int64_t n_out,
+                                       double eps, void* out, void* stream) {
+    static const char* fn = "lwg_add_norm_gather";
+    int32_t st;
+    if ((st = check_width(fn, C)) || (st = check_eps(fn, eps)) || (st = check_rows(fn, "n_src", n_src)) ||
+        (st = check_rows(fn, "n_out", n_out)))
+        return st;
+    if (n_out == 0) return ok();
+    if ((st = check_table_ptr(fn, "table", table)) || (st = check_tensor(fn, "out", out))) return st;
+    if (n_src > 0 && ((st = check_tensor(fn, "branch", branch)) || (st = check_tensor(fn, "residual", residual)) ||
+                      (st = check_tensor(fn, "residual_out", residual_out))))
+        return st;
+    const uint64_t src_bytes = static_cast<uint64_t>(n_src) * C * 2;
+    const uint64_t out_bytes = static_cast<uint64_t>(n_out) * C * 2;
+    const uint64_t table_bytes = static_cast<uint64_t>(n_out) * 4;
+    if (overlap(out, out_bytes, table, table_bytes))
+        return fail(LWG_ERR_ALIASING, "%s: out overlaps table", fn);
+    if (n_src > 0) {
+        if (overlap(out, out_bytes, branch, src_bytes) || overlap(out, out_bytes, residual, src_bytes) ||
+            overlap(out, out_bytes, residual_out, src_bytes))
+            return fail(LWG_ERR_ALIASING, "%s: out overlaps a token tensor", fn);
+        if (!same_or_disjoint(residual_out, residual, src_bytes) ||
+            !same_or_disjoint(residual_out, branch, src_bytes) ||
+            overlap(residual_out, src_bytes, table, table_bytes))
+            return fail(LWG_ERR_ALIASING, "%s: residual_out partially overlaps an input", fn);
+    }
+    return hip_result(lwg::launch_add_norm_gather(branch, residual, residual_out, n_src, C, table, n_out, eps,
+                                                  out, static_cast<hipStream_t>(stream)),
                       fn);
 }

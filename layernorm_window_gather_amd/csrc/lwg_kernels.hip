@@ -156,6 +156,15 @@ __device__ __forceinline__ void residual_add(const chunk_t (&branch)[K], chunk_t
     }
 }
 
+// 1/sqrt(a) for a > 0: the hardware reciprocal-square-root estimate refined by
+// one Newton step, r' = r (3/2 - a r^2 / 2), which roughly squares its relative
+// error and lands within a few ulp of the binary64 result. Inf and NaN give NaN.
+__device__ __forceinline__ double rsqrt_refined(double a) {
+    const double r = __builtin_amdgcn_rsq(a);
+    const double h = 0.5 * a * r;
+    return __builtin_fma(r, __builtin_fma(-h, r, 0.5), r);
+}
+
 // LayerNorm of the row whose 1/LPR share this lane holds in v (section 3):
 // mean, biased variance of the deviations (two passes over registers), then
 // (x - mean) / sqrt(var + eps) rounded to binary16, written back into v.
@@ -164,6 +173,7 @@ __device__ __forceinline__ void residual_add(const chunk_t (&branch)[K], chunk_t
 template <int C, int K>
 __device__ __forceinline__ void layer_norm_lane(chunk_t (&v)[K], double eps) {
     using T = Tile<C, K>;
+    constexpr double kInvC = 1.0 / C;
     double x[T::kValues];
 #pragma unroll
     for (int k = 0; k < K; ++k) unpack8(v[k], x + 8 * k);
@@ -174,25 +184,24 @@ __device__ __forceinline__ void layer_norm_lane(chunk_t (&v)[K], double eps) {
         s0 += x[i];
         s1 += x[i + 1];
     }
-    const double mean = group_sum<T::kLanes>(s0 + s1) / static_cast<double>(C);
+    const double mean = group_sum<T::kLanes>(s0 + s1) * kInvC;
 
+    // x becomes the deviation from the mean; its squares give the variance
     double q0 = 0.0, q1 = 0.0;
 #pragma unroll
     for (int i = 0; i < T::kValues; i += 2) {
-        const double d0 = x[i] - mean, d1 = x[i + 1] - mean;
-        q0 = __builtin_fma(d0, d0, q0);
-        q1 = __builtin_fma(d1, d1, q1);
+        x[i] -= mean;
+        x[i + 1] -= mean;
+        q0 = __builtin_fma(x[i], x[i], q0);
+        q1 = __builtin_fma(x[i + 1], x[i + 1], q1);
     }
-    const double var = group_sum<T::kLanes>(q0 + q1) / static_cast<double>(C);
-    const double rstd = 1.0 / __builtin_sqrt(var + eps);
+    const double rstd = rsqrt_refined(group_sum<T::kLanes>(q0 + q1) * kInvC + eps);
 
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         const double* xk = x + 8 * k;
-        v[k] = chunk_t{pack2((xk[0] - mean) * rstd, (xk[1] - mean) * rstd),
-                       pack2((xk[2] - mean) * rstd, (xk[3] - mean) * rstd),
-                       pack2((xk[4] - mean) * rstd, (xk[5] - mean) * rstd),
-                       pack2((xk[6] - mean) * rstd, (xk[7] - mean) * rstd)};
+        v[k] = chunk_t{pack2(xk[0] * rstd, xk[1] * rstd), pack2(xk[2] * rstd, xk[3] * rstd),
+                       pack2(xk[4] * rstd, xk[5] * rstd), pack2(xk[6] * rstd, xk[7] * rstd)};
     }
 }
 
@@ -312,6 +321,92 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(const chunk_t* __restric
     }
 }
 
+// Window reverse fused with the residual add + LayerNorm: token row i takes
+// its branch from window row idx[i] (the inverse table), adds the residual,
+// writes the rounded sum, and normalises it. An index outside [0, n_win) gives
+// a zero branch. residual_out and y may alias residual (row i is read and
+// written by the same lanes).
+template <int C, int K, class H>
+__global__ __launch_bounds__(kBlock) void reverse_add_ln_kernel(
+    const chunk_t* __restrict__ win, int64_t n_win, const int32_t* __restrict__ idx,
+    const chunk_t* residual, chunk_t* residual_out, chunk_t* y, int64_t rows, double eps) {
+    using T = Tile<C, K>;
+    const int lane = threadIdx.x & 63;
+    const int sub = lane % T::kLanes;
+    for (int64_t w = first_wave<T>(); w * T::kRowsPerWave < rows; w += wave_stride()) {
+        const int64_t row = w * T::kRowsPerWave + lane / T::kLanes;
+        const bool live = row < rows;
+        const int32_t t = live ? idx[row] : -1;
+        const bool valid = t >= 0 && static_cast<int64_t>(t) < n_win;
+        const int64_t base = row * T::kChunks + sub;
+        const int64_t src = static_cast<int64_t>(t) * T::kChunks + sub;
+        chunk_t b[K], r[K];
+        zero(b);
+        zero(r);
+        if (valid) {
+#pragma unroll
+            for (int k = 0; k < K; ++k) b[k] = load16<H>(win + src + k * T::kLanes);
+        }
+        if (live) {
+#pragma unroll
+            for (int k = 0; k < K; ++k) r[k] = load16<H>(residual + base + k * T::kLanes);
+        }
+        residual_add<K>(b, r);
+        if (live) {
+#pragma unroll
+            for (int k = 0; k < K; ++k) store16<H>(residual_out + base + k * T::kLanes, r[k]);
+        }
+        layer_norm_lane<C, K>(r, eps);
+        if (live) {
+#pragma unroll
+            for (int k = 0; k < K; ++k) store16<H>(y + base + k * T::kLanes, r[k]);
+        }
+    }
+}
+
+// Residual add + LayerNorm + window gather, output-major: gathered row j reads
+// token t = table[j] from branch and residual, writes the rounded sum to
+// residual_out[t] and its LayerNorm to out[j]; padding rows store +0.0 and
+// touch no token. With a table whose valid entries are distinct (as built by
+// window_index_kernel) every token row is read and written by exactly one lane
+// group, so residual_out may alias residual or branch.
+template <int C, int K, class H>
+__global__ __launch_bounds__(kBlock) void add_norm_gather_kernel(
+    const chunk_t* branch, const chunk_t* residual, chunk_t* residual_out, int64_t n_src,
+    const int32_t* __restrict__ table, int64_t n_out, chunk_t* __restrict__ out, double eps) {
+    using T = Tile<C, K>;
+    const int lane = threadIdx.x & 63;
+    const int sub = lane % T::kLanes;
+    for (int64_t w = first_wave<T>(); w * T::kRowsPerWave < n_out; w += wave_stride()) {
+        const int64_t j = w * T::kRowsPerWave + lane / T::kLanes;
+        const bool live = j < n_out;
+        const int32_t t = live ? table[j] : -1;
+        const bool valid = t >= 0 && static_cast<int64_t>(t) < n_src;
+        const int64_t src = static_cast<int64_t>(t) * T::kChunks + sub;
+        chunk_t b[K], r[K];
+        zero(b);
+        zero(r);
+        if (valid) {
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                b[k] = load16<H>(branch + src + k * T::kLanes);
+                r[k] = load16<H>(residual + src + k * T::kLanes);
+            }
+        }
+        residual_add<K>(b, r);
+        if (valid) {
+#pragma unroll
+            for (int k = 0; k < K; ++k) store16<H>(residual_out + src + k * T::kLanes, r[k]);
+        }
+        layer_norm_lane<C, K>(r, eps);
+        if (live) {
+            const int64_t dst = j * T::kChunks + sub;
+#pragma unroll
+            for (int k = 0; k < K; ++k) store16<H>(out + dst + k * T::kLanes, r[k]);
+        }
+    }
+}
+
 __device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
     return static_cast<uint32_t>((static_cast<uint64_t>(n) * f.m) >> f.s);
 }
@@ -346,6 +441,28 @@ __global__ __launch_bounds__(kBlock) void window_index_kernel(WindowGeometry g, 
                    : -1;
 }
 
+// One thread per source token i = (z*H + h)*W + w: its rolled position is
+// g = (q - s) mod padded extent on each axis (the inverse of the forward
+// table's q = (p + s) mod padded extent); the gathered row holding it is the
+// window of g times the window volume plus g's offset inside the window.
+__global__ __launch_bounds__(kBlock) void window_inverse_kernel(WindowGeometry g, int32_t* inverse) {
+    const uint32_t i = blockIdx.x * kBlock + threadIdx.x;
+    const uint32_t tokens = static_cast<uint32_t>(g.Z) * g.H * g.W;
+    if (i >= tokens) return;
+    const uint32_t zh = fdiv(i, g.div_W);
+    const uint32_t w = i - zh * g.W;
+    const uint32_t z = fdiv(zh, g.div_H);
+    const uint32_t h = zh - z * g.H;
+    // q < real extent <= padded extent and s < padded extent
+    const uint32_t gz = z >= static_cast<uint32_t>(g.sz) ? z - g.sz : z + g.Zp - g.sz;
+    const uint32_t gh = h >= static_cast<uint32_t>(g.sh) ? h - g.sh : h + g.Hp - g.sh;
+    const uint32_t gw = w >= static_cast<uint32_t>(g.sw) ? w - g.sw : w + g.Wp - g.sw;
+    const uint32_t bz = fdiv(gz, g.div_wz), bh = fdiv(gh, g.div_wh), bw = fdiv(gw, g.div_ww);
+    const uint32_t dz = gz - bz * g.wz, dh = gh - bh * g.wh, dw = gw - bw * g.ww;
+    const uint32_t window = (bz * g.nbh + bh) * g.nbw + bw;
+    inverse[i] = static_cast<int32_t>(window * g.win_tokens + (dz * g.wh + dh) * g.ww + dw);
+}
+
 // ---------------------------------------------------------------------------
 // Launch configuration
 
@@ -363,7 +480,7 @@ __global__ __launch_bounds__(kBlock) void window_index_kernel(WindowGeometry g, 
 // and store-only-hinted accesses for every kernel. The grid is one tile per
 // wave, except the C = 384 norm-gather, which is capped at 4 workgroups per
 // compute unit with each wave looping over tiles.
-enum class Op { kLn, kAddLn, kGather, kNormGather };
+enum class Op { kLn, kAddLn, kGather, kNormGather, kReverseAddLn, kAddNormGather };
 
 template <int C> struct Width;
 template <> struct Width<192> { static constexpr int K = 3; };
@@ -455,6 +572,49 @@ hipError_t launch_norm_gather(const void* x, int64_t n_src, int32_t C, const int
                               int64_t n_out, double eps, void* out, hipStream_t stream) {
     return C == 192 ? gather_c<192, true>(x, n_src, table, n_out, eps, out, stream)
                     : gather_c<384, true>(x, n_src, table, n_out, eps, out, stream);
+}
+
+hipError_t launch_window_inverse(const WindowGeometry& g, int32_t* inverse, hipStream_t stream) {
+    const int64_t tokens = static_cast<int64_t>(g.Z) * g.H * g.W;
+    const unsigned grid = static_cast<unsigned>((tokens + kBlock - 1) / kBlock);
+    window_inverse_kernel<<<grid, kBlock, 0, stream>>>(g, inverse);
+    return hipGetLastError();
+}
+
+template <int C>
+hipError_t reverse_add_ln_c(const void* win, int64_t n_win, const int32_t* idx, const void* r, void* ro,
+                            void* y, int64_t rows, double eps, hipStream_t s) {
+    using L = Launch<C, Op::kReverseAddLn>;
+    reverse_add_ln_kernel<C, Width<C>::K, typename L::H>
+        <<<grid_for<C, Op::kReverseAddLn>(rows), kBlock, 0, s>>>(
+            static_cast<const chunk_t*>(win), n_win, idx, static_cast<const chunk_t*>(r),
+            static_cast<chunk_t*>(ro), static_cast<chunk_t*>(y), rows, eps);
+    return hipGetLastError();
+}
+
+hipError_t launch_reverse_add_ln(const void* win, int64_t n_win, const int32_t* inverse,
+                                 const void* residual, void* residual_out, void* y, int64_t rows,
+                                 int32_t C, double eps, hipStream_t stream) {
+    return C == 192 ? reverse_add_ln_c<192>(win, n_win, inverse, residual, residual_out, y, rows, eps, stream)
+                    : reverse_add_ln_c<384>(win, n_win, inverse, residual, residual_out, y, rows, eps, stream);
+}
+
+template <int C>
+hipError_t add_norm_gather_c(const void* b, const void* r, void* ro, int64_t n_src, const int32_t* table,
+                             int64_t n_out, double eps, void* out, hipStream_t s) {
+    using L = Launch<C, Op::kAddNormGather>;
+    add_norm_gather_kernel<C, Width<C>::K, typename L::H>
+        <<<grid_for<C, Op::kAddNormGather>(n_out), kBlock, 0, s>>>(
+            static_cast<const chunk_t*>(b), static_cast<const chunk_t*>(r), static_cast<chunk_t*>(ro),
+            n_src, table, n_out, static_cast<chunk_t*>(out), eps);
+    return hipGetLastError();
+}
+
+hipError_t launch_add_norm_gather(const void* branch, const void* residual, void* residual_out,
+                                  int64_t n_src, int32_t C, const int32_t* table, int64_t n_out,
+                                  double eps, void* out, hipStream_t stream) {
+    return C == 192 ? add_norm_gather_c<192>(branch, residual, residual_out, n_src, table, n_out, eps, out, stream)
+                    : add_norm_gather_c<384>(branch, residual, residual_out, n_src, table, n_out, eps, out, stream);
 }
 
 }  // namespace lwg

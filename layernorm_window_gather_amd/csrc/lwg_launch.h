@@ -37,7 +37,8 @@ struct WindowGeometry {
     int32_t nbh, nbw;       // windows along h and w
     int32_t win_tokens;     // wz * wh * ww
     int32_t rows;           // Zp * Hp * Wp
-    FastDiv div_win, div_nbw, div_nbh, div_ww, div_wh;
+    FastDiv div_win, div_nbw, div_nbh, div_ww, div_wh;  // forward table
+    FastDiv div_W, div_H, div_wz;                        // inverse table
 };
 
 hipError_t launch_ln_fixed(const void* x, void* y, int64_t rows, int32_t C, double eps,
@@ -49,6 +50,13 @@ hipError_t launch_window_gather(const void* x, int64_t n_src, int32_t C, const i
                                 int64_t n_out, void* out, hipStream_t stream);
 hipError_t launch_norm_gather(const void* x, int64_t n_src, int32_t C, const int32_t* table,
                               int64_t n_out, double eps, void* out, hipStream_t stream);
+hipError_t launch_window_inverse(const WindowGeometry& g, int32_t* inverse, hipStream_t stream);
+hipError_t launch_reverse_add_ln(const void* win, int64_t n_win, const int32_t* inverse,
+                                 const void* residual, void* residual_out, void* y, int64_t rows,
+                                 int32_t C, double eps, hipStream_t stream);
+hipError_t launch_add_norm_gather(const void* branch, const void* residual, void* residual_out,
+                                  int64_t n_src, int32_t C, const int32_t* table, int64_t n_out,
+                                  double eps, void* out, hipStream_t stream);
 
 }  // namespace lwg
 

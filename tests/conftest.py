@@ -15,3 +15,13 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def golden_dir():
     return os.path.join(ROOT, "tests", "golden")
+
+
+@pytest.fixture(scope="session")
+def dev():
+    """cuda:0 with the in-tree liblwg.so loaded; GPU tests fail (not skip) without them."""
+    import torch
+    import layernorm_window_gather_amd as lwg
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    lwg.library()
+    return torch.device("cuda", 0)

@@ -176,3 +176,48 @@ def test_error_carries_status_and_message():
         _lib.check(_lib.load().lwg_ln_fixed(A16, B16, 10, 100, 1e-5, ST))
     assert e.value.status == _lib.LWG_ERR_UNSUPPORTED_WIDTH
     assert "C=100" in str(e.value)
+
+
+def test_inverse_build_validation(lib):
+    S = _lib
+    f = lib.lwg_window_inverse_build
+    assert f(8, 182, 90, 2, 6, 12, 1, 3, 6, A16, 131039, ST) == S.LWG_ERR_SIZE_MISMATCH
+    assert f(8, 182, 90, 2, 6, 12, 1, 3, 6, A16, 142848, ST) == S.LWG_ERR_SIZE_MISMATCH
+    assert f(8, 182, 90, 2, 0, 12, 1, 3, 6, A16, 131040, ST) == S.LWG_ERR_INVALID_ARGUMENT
+    assert f(8, 182, 90, 2, 6, 12, 1, -3, 6, A16, 131040, ST) == S.LWG_ERR_INVALID_ARGUMENT
+    assert f(8, 182, 90, 2, 6, 12, 1, 3, 6, None, 131040, ST) == S.LWG_ERR_INVALID_ARGUMENT
+    assert f(8, 182, 90, 2, 6, 12, 1, 3, 6, P(0x10001), 131040, ST) == S.LWG_ERR_MISALIGNED
+    assert f(0, 182, 90, 2, 6, 12, 1, 3, 6, None, 0, ST) == S.LWG_OK
+
+
+def test_reverse_add_ln_validation(lib):
+    S = _lib
+    f = lib.lwg_window_reverse_add_ln
+    W, I, R, RO, Y = P(0x100000), P(0x200000), P(0x300000), P(0x400000), P(0x500000)
+    assert f(W, 200, I, R, RO, Y, 100, 128, 1e-5, ST) == S.LWG_ERR_UNSUPPORTED_WIDTH
+    assert f(W, 200, I, R, RO, Y, 100, 192, 0.0, ST) == S.LWG_ERR_INVALID_ARGUMENT
+    assert f(W, -1, I, R, RO, Y, 100, 192, 1e-5, ST) == S.LWG_ERR_INVALID_ARGUMENT
+    assert f(W, 200, None, R, RO, Y, 100, 192, 1e-5, ST) == S.LWG_ERR_INVALID_ARGUMENT
+    assert f(W, 200, P(0x200002), R, RO, Y, 100, 192, 1e-5, ST) == S.LWG_ERR_MISALIGNED
+    assert f(None, 200, I, R, RO, Y, 100, 192, 1e-5, ST) == S.LWG_ERR_INVALID_ARGUMENT
+    assert f(W, 200, I, R, RO, RO, 100, 192, 1e-5, ST) == S.LWG_ERR_ALIASING        # y == residual_out
+    assert f(W, 200, I, R, P(0x300000 + 384), Y, 100, 192, 1e-5, ST) == S.LWG_ERR_ALIASING
+    assert f(W, 200, I, R, P(0x100000 + 384), Y, 100, 192, 1e-5, ST) == S.LWG_ERR_ALIASING  # into win
+    assert f(W, 200, I, R, RO, P(0x200000 - 16), 100, 192, 1e-5, ST) == S.LWG_ERR_ALIASING  # onto inverse
+    assert f(None, 0, None, None, None, None, 0, 192, 1e-5, ST) == S.LWG_OK
+
+
+def test_add_norm_gather_validation(lib):
+    S = _lib
+    f = lib.lwg_add_norm_gather
+    B, R, RO, T, O = P(0x100000), P(0x200000), P(0x300000), P(0x400000), P(0x500000)
+    assert f(B, R, RO, 100, 200, T, 150, 1e-5, O, ST) == S.LWG_ERR_UNSUPPORTED_WIDTH
+    assert f(B, R, RO, 100, 192, T, 150, float("nan"), O, ST) == S.LWG_ERR_INVALID_ARGUMENT
+    assert f(B, R, RO, -5, 192, T, 150, 1e-5, O, ST) == S.LWG_ERR_INVALID_ARGUMENT
+    assert f(B, R, RO, 100, 192, None, 150, 1e-5, O, ST) == S.LWG_ERR_INVALID_ARGUMENT
+    assert f(B, None, RO, 100, 192, T, 150, 1e-5, O, ST) == S.LWG_ERR_INVALID_ARGUMENT
+    assert f(B, R, RO, 100, 192, T, 150, 1e-5, MIS, ST) == S.LWG_ERR_MISALIGNED
+    assert f(B, R, RO, 100, 192, T, 150, 1e-5, P(0x100000 + 384), ST) == S.LWG_ERR_ALIASING   # out on branch
+    assert f(B, R, RO, 100, 192, T, 150, 1e-5, P(0x400000 - 16), ST) == S.LWG_ERR_ALIASING    # out on table
+    assert f(B, R, P(0x200000 + 768), 100, 192, T, 150, 1e-5, O, ST) == S.LWG_ERR_ALIASING    # partial
+    assert f(None, None, None, 0, 192, None, 0, 1e-5, None, ST) == S.LWG_OK

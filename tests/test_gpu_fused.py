@@ -1,0 +1,144 @@
+"""Parity of the window reverse and the two fusions around the window gather
+(reverse + add + LayerNorm, add + LayerNorm + gather) with the CPU oracle, at
+small ragged sizes and at the level-1 / level-2 shapes."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from workloads import LEVEL1, LEVEL2, WINDOW, SHIFT, NO_SHIFT
+
+from parity_helpers import assert_bit_exact, assert_ln_close, bits, host, to_dev
+
+torch = pytest.importorskip("torch")
+lwg = pytest.importorskip("layernorm_window_gather_amd")
+
+pytestmark = pytest.mark.gpu
+
+GRIDS = [((2, 12, 24), NO_SHIFT), ((2, 12, 24), SHIFT), ((2, 7, 13), SHIFT), ((4, 9, 26), (3, 13, 30)),
+         ((1, 1, 1), SHIFT), ((5, 11, 25), (0, 5, 11))]
+
+
+@pytest.mark.parametrize("grid,shift", GRIDS + [(LEVEL1.grid, SHIFT), (LEVEL2.grid, NO_SHIFT), (LEVEL2.grid, SHIFT)])
+def test_window_inverse_build_bit_exact(dev, grid, shift):
+    inv = host(lwg.window_inverse_build(grid, WINDOW, shift, device=dev))
+    assert inv.dtype == np.int32
+    assert np.array_equal(inv, oracle.window_inverse_table(grid, WINDOW, shift))
+
+
+@pytest.mark.parametrize("C", [192, 384])
+@pytest.mark.parametrize("grid,shift", GRIDS[:4])
+def test_window_reverse_round_trip(dev, C, grid, shift):
+    n = int(np.prod(grid))
+    x = workloads.normal_rows(81, n, C)
+    t = lwg.window_index_build(grid, WINDOW, shift, device=dev)
+    inv = lwg.window_inverse_build(grid, WINDOW, shift, device=dev)
+    g = lwg.window_gather(to_dev(x, dev), t)
+    back = host(lwg.window_reverse(g, inv))
+    assert_bit_exact(back, x, "gather then reverse")
+    rows = workloads.normal_rows(82, t.numel(), C)
+    assert_bit_exact(host(lwg.window_reverse(to_dev(rows, dev), inv)),
+                     oracle.window_reverse(rows, grid, WINDOW, shift), "reverse vs oracle")
+
+
+@pytest.mark.parametrize("C", [192, 384])
+@pytest.mark.parametrize("grid,shift", GRIDS)
+def test_window_reverse_add_ln_small(dev, C, grid, shift):
+    n = int(np.prod(grid))
+    m = oracle.window_token_count(grid, WINDOW)
+    rows = workloads.normal_rows(83, m, C, std=2.0)
+    res = workloads.normal_rows(84, n, C)
+    inv = lwg.window_inverse_build(grid, WINDOW, shift, device=dev)
+    r, y = lwg.window_reverse_add_ln(to_dev(rows, dev), inv, to_dev(res, dev))
+    r_ref, y_ref = oracle.window_reverse_add_ln(rows, res, grid, WINDOW, shift)
+    assert_bit_exact(host(r), r_ref, f"reverse_add_ln residual C={C} grid={grid}")
+    assert_ln_close(host(y), y_ref, f"reverse_add_ln C={C} grid={grid}")
+
+
+@pytest.mark.parametrize("C", [192, 384])
+def test_window_reverse_add_ln_in_place_and_composition(dev, C):
+    grid, shift = (4, 9, 26), SHIFT
+    n, m = int(np.prod(grid)), oracle.window_token_count(grid, WINDOW)
+    rows = workloads.normal_rows(85, m, C)
+    res = workloads.normal_rows(86, n, C, mean=100.0)
+    inv = lwg.window_inverse_build(grid, WINDOW, shift, device=dev)
+    tr, trows = to_dev(res, dev), to_dev(rows, dev)
+    r_ref, y_ref = oracle.window_reverse_add_ln(rows, res, grid, WINDOW, shift)
+    # composition: the fused call equals reverse, then add_ln
+    r2, y2 = lwg.add_ln(lwg.window_reverse(trows, inv), tr)
+    r1, y1 = lwg.window_reverse_add_ln(trows, inv, tr)
+    assert_bit_exact(host(r1), host(r2), "fused residual vs reverse then add_ln")
+    assert_bit_exact(host(y1), host(y2), "fused y vs reverse then add_ln")
+    # residual stream updated in place
+    lwg.window_reverse_add_ln(trows, inv, tr, residual_out=tr)
+    assert_bit_exact(host(tr), r_ref, "in-place residual")
+    assert_ln_close(host(y1), y_ref, "reverse_add_ln y")
+
+
+@pytest.mark.parametrize("C", [192, 384])
+@pytest.mark.parametrize("grid,shift", GRIDS)
+def test_add_norm_gather_small(dev, C, grid, shift):
+    n = int(np.prod(grid))
+    br = workloads.normal_rows(87, n, C)
+    res = workloads.normal_rows(88, n, C, std=3.0)
+    t = lwg.window_index_build(grid, WINDOW, shift, device=dev)
+    table = oracle.window_index_table(grid, WINDOW, shift)
+    r, out = lwg.add_norm_gather(to_dev(br, dev), to_dev(res, dev), t)
+    r_ref, out_ref = oracle.add_norm_gather(br, res, table)
+    assert_bit_exact(host(r), r_ref, f"add_norm_gather residual C={C} grid={grid}")
+    g = host(out)
+    assert_ln_close(g, out_ref, f"add_norm_gather C={C} grid={grid}")
+    assert not bits(g[table < 0]).any()
+
+
+@pytest.mark.parametrize("C", [192, 384])
+def test_add_norm_gather_aliasing_and_composition(dev, C):
+    grid, shift = (4, 9, 26), SHIFT
+    n = int(np.prod(grid))
+    br = workloads.normal_rows(89, n, C)
+    res = workloads.normal_rows(90, n, C)
+    t = lwg.window_index_build(grid, WINDOW, shift, device=dev)
+    table = oracle.window_index_table(grid, WINDOW, shift)
+    r_ref, out_ref = oracle.add_norm_gather(br, res, table)
+    tb, tr = to_dev(br, dev), to_dev(res, dev)
+    r_sep, _ = lwg.add_ln(tb, tr)
+    composed = host(lwg.norm_gather(r_sep, t))
+    r1, o1 = lwg.add_norm_gather(tb, tr, t)
+    assert_bit_exact(host(o1), composed, "fused vs add_ln then norm_gather")
+    lwg.add_norm_gather(tb, tr, t, residual_out=tr)          # in place on the residual
+    assert_bit_exact(host(tr), r_ref, "in-place residual")
+    tb, tr = to_dev(br, dev), to_dev(res, dev)
+    lwg.add_norm_gather(tb, tr, t, residual_out=tb)          # written over the branch
+    assert_bit_exact(host(tb), r_ref, "residual over the branch")
+    assert_ln_close(host(o1), out_ref, "add_norm_gather out")
+
+
+@pytest.mark.parametrize("level,seed", [(LEVEL1, 91), (LEVEL2, 92)])
+def test_fused_rows_full_size(dev, level, seed):
+    n, c = level.tokens, level.channels
+    m = oracle.window_token_count(level.grid, WINDOW)
+    nc, off = workloads.stress_row_classes(seed, n)
+    res = workloads.mixed_rows(seed + 1, n, c, nc, off)
+    br = workloads.mixed_rows(seed + 2, n, c, nc, off, offset_mean=0.0)
+    attn = workloads.normal_rows(seed + 3, m, c)
+    table = oracle.window_index_table(level.grid, WINDOW, SHIFT)
+    t = lwg.window_index_build(level.grid, WINDOW, SHIFT, device=dev)
+    inv = lwg.window_inverse_build(level.grid, WINDOW, SHIFT, device=dev)
+    r, y = lwg.window_reverse_add_ln(to_dev(attn, dev), inv, to_dev(res, dev))
+    r_ref, y_ref = oracle.window_reverse_add_ln(attn, res, level.grid, WINDOW, SHIFT)
+    assert_bit_exact(host(r), r_ref, f"reverse_add_ln residual {level.name}")
+    assert_ln_close(host(y), y_ref, f"reverse_add_ln {level.name}")
+    r2, g = lwg.add_norm_gather(to_dev(br, dev), to_dev(res, dev), t)
+    r2_ref, g_ref = oracle.add_norm_gather(br, res, table)
+    assert_bit_exact(host(r2), r2_ref, f"add_norm_gather residual {level.name}")
+    gh = host(g)
+    assert_ln_close(gh, g_ref, f"add_norm_gather {level.name}")
+    assert not bits(gh[table < 0]).any()
+
+
+@pytest.mark.parametrize("window", [(1, 1, 1), (3, 5, 7), (8, 7, 7)])
+def test_window_inverse_other_windows(dev, window):
+    grid = (6, 17, 31)
+    for shift in [(0, 0, 0), (1, 2, 3), (5, 40, 100)]:
+        inv = host(lwg.window_inverse_build(grid, window, shift, device=dev))
+        assert np.array_equal(inv, oracle.window_inverse_table(grid, window, shift)), (window, shift)

@@ -19,52 +19,7 @@ lwg = pytest.importorskip("layernorm_window_gather_amd")
 
 pytestmark = pytest.mark.gpu
 
-MAX_ABS, MEAN_ABS = 2e-3, 1e-4
-
-
-@pytest.fixture(scope="module")
-def dev():
-    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
-    lwg.library()  # the in-tree liblwg.so; raises if it was not built
-    return torch.device("cuda", 0)
-
-
-def to_dev(a, dev):
-    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
-
-
-def host(t):
-    torch.cuda.synchronize()
-    return t.cpu().numpy()
-
-
-def bits(a):
-    return np.asarray(a, dtype=np.float16).view(np.uint16)
-
-
-def assert_bit_exact(got, ref, label=""):
-    g, r = bits(got), bits(ref)
-    assert g.shape == r.shape, label
-    bad = np.flatnonzero(g.reshape(-1) != r.reshape(-1))
-    assert bad.size == 0, f"{label}: {bad.size} elements differ, first at flat index {bad[:5]}"
-
-
-def assert_ln_close(got, ref, label="", max_mismatch_frac=1e-6):
-    g = np.asarray(got, np.float16).astype(np.float64)
-    r = np.asarray(ref, np.float16).astype(np.float64)
-    assert g.shape == r.shape, label
-    nan_r = np.isnan(r)
-    assert np.array_equal(np.isnan(g), nan_r), f"{label}: NaN positions differ"
-    d = np.abs(g[~nan_r] - r[~nan_r])
-    if d.size == 0:
-        return 0
-    mismatches = int((d > 0).sum())
-    print(f"[{label}] max_abs={d.max():.3e} mean_abs={d.mean():.3e} "
-          f"mismatches={mismatches}/{d.size}", flush=True)
-    assert d.max() <= MAX_ABS, f"{label}: max-abs {d.max()}"
-    assert d.mean() <= MEAN_ABS, f"{label}: mean-abs {d.mean()}"
-    assert mismatches <= max(2, max_mismatch_frac * d.size), f"{label}: {mismatches} mismatches"
-    return mismatches
+from parity_helpers import MAX_ABS, MEAN_ABS, assert_bit_exact, assert_ln_close, bits, host, to_dev  # noqa: E402,F401
 
 
 RAGGED_ROWS = [1, 3, 7, 8, 9, 15, 16, 17, 63, 64, 65, 127, 129, 1000, 4097]
