@@ -11,7 +11,10 @@ Everything is plain numpy in float64, written from the definitions on the page
 
 * ``residual_sum`` -- section 4 (fused residual add + norm: the residual is
   rounded to FP16 once, before the normalisation reads it);
-* ``layer_norm`` -- section 3 (fixed-width LayerNorm, no affine, widths 192/384);
+* ``layer_norm`` -- section 3 (fixed-width LayerNorm, no affine, widths 192/384,
+  plus the patch-merge width 768);
+* ``layer_norm_affine`` / ``add_ln_affine`` -- the same with a per-channel scale
+  and shift, for callers that do not fold them into the next Linear;
 * ``window_token_count`` / ``window_index_table`` -- section 5 (INT32 index
   table per window shape, padding folded into the index protocol);
 * ``window_gather`` -- section 5 (index >= 0 copies the source token, -1 writes
@@ -27,13 +30,15 @@ Each function is pinned by ``tests/test_oracle_pins.py`` to closed forms,
 brute force on tiny inputs, a library routine, or values derived by hand and
 stored under ``tests/golden/``.
 """
-from .rowops import EPS, WIDTHS, fp16_round, residual_sum, layer_norm, add_ln
+from .rowops import (EPS, WIDTHS, fp16_round, residual_sum, layer_norm, add_ln, layer_norm_affine,
+                     add_ln_affine)
 from .window import (padded_extent, window_token_count, window_index_table,
                      window_gather, norm_gather, norm_gather_rows, window_reverse,
                      window_inverse_table, window_reverse_add_ln, add_norm_gather)
 
 __all__ = [
-    "EPS", "WIDTHS", "fp16_round", "residual_sum", "layer_norm", "add_ln",
+    "EPS", "WIDTHS", "fp16_round", "residual_sum", "layer_norm", "add_ln", "layer_norm_affine",
+    "add_ln_affine",
     "padded_extent", "window_token_count", "window_index_table", "window_gather",
     "norm_gather", "norm_gather_rows", "window_reverse", "window_inverse_table",
     "window_reverse_add_ln", "add_norm_gather",

@@ -9,9 +9,11 @@ import numpy as np
 # LayerNorm epsilon; the pages give none, 1e-5 is the framework default that the
 # replaced native_layer_norm calls used.
 EPS = 1e-5
-# Section 3 of the BW1000 page: the model's hidden widths are only 192 and 384;
-# any other width is refused rather than served by an untested path.
-WIDTHS = (192, 384)
+# Section 3 of the BW1000 page: the model's hidden widths are 192 and 384, and
+# any width without its own tests is refused rather than served by an untested
+# path. 768 is the patch-merge width of the same model (four neighbouring
+# 192-channel tokens concatenated before the merge), added with its own tests.
+WIDTHS = (192, 384, 768)
 
 
 def fp16_round(values) -> np.ndarray:
@@ -59,3 +61,32 @@ def add_ln(branch: np.ndarray, residual: np.ndarray, eps: float = EPS):
     LayerNorm reads that rounded residual. Returns (residual_out, y)."""
     r = residual_sum(residual, branch)
     return r, layer_norm(r, eps)
+
+
+def layer_norm_affine(x: np.ndarray, gamma: np.ndarray, beta: np.ndarray, eps: float = EPS) -> np.ndarray:
+    """LayerNorm with a per-channel scale and shift, for callers that do not fold
+    the affine parameters into the next Linear (section 3 of the BW1000 page
+    folds them; this is the unfolded form): y = (x - mean) / sqrt(var + eps) *
+    gamma + beta, computed in float64 from binary16 x, gamma and beta, rounded
+    once to binary16."""
+    a = np.asarray(x, dtype=np.float16)
+    if a.ndim != 2 or a.shape[1] not in WIDTHS:
+        raise ValueError(f"layer_norm_affine expects [rows, C] with C in {WIDTHS}, got {a.shape}")
+    g = np.asarray(gamma, dtype=np.float16).astype(np.float64).reshape(1, -1)
+    b = np.asarray(beta, dtype=np.float16).astype(np.float64).reshape(1, -1)
+    if g.shape[1] != a.shape[1] or b.shape[1] != a.shape[1]:
+        raise ValueError("gamma and beta must have one entry per channel")
+    v = a.astype(np.float64)
+    with np.errstate(invalid="ignore", over="ignore"):
+        mean = v.mean(axis=1, keepdims=True)
+        dev = v - mean
+        var = (dev * dev).mean(axis=1, keepdims=True)
+        y = dev / np.sqrt(var + eps) * g + b
+    return fp16_round(y)
+
+
+def add_ln_affine(branch: np.ndarray, residual: np.ndarray, gamma: np.ndarray, beta: np.ndarray,
+                  eps: float = EPS):
+    """Residual add (section 4) followed by the affine LayerNorm. Returns (residual_out, y)."""
+    r = residual_sum(residual, branch)
+    return r, layer_norm_affine(r, gamma, beta, eps)

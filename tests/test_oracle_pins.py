@@ -395,3 +395,74 @@ def test_window_reverse_add_ln_and_add_norm_gather_compose():
     r2, g = oracle.add_norm_gather(br, res, t)
     assert np.array_equal(bits_of(r2), bits_of(oracle.residual_sum(res, br)))
     assert np.array_equal(bits_of(g), bits_of(oracle.window_gather(oracle.layer_norm(r2), t)))
+
+
+# ---------------------------------------------------------------------------
+# the patch-merge width and the affine LayerNorm
+
+
+def test_ln_width_768_closed_forms():
+    C = 768
+    row = np.array([1.0] * (C // 2) + [-1.0] * (C // 2), dtype=np.float16)[None, :]
+    assert (bits_of(oracle.layer_norm(row))[0, : C // 2] == 0x3C00).all()
+    k, a, b = 100, 3.0, -0.5
+    row = np.array([a] * k + [b] * (C - k), dtype=np.float16)[None, :]
+    ya, yb = _two_valued_expected(C, k, a, b)
+    y = oracle.layer_norm(row)
+    assert (bits_of(y[0, :k]) == bits_of(ya)).all() and (bits_of(y[0, k:]) == bits_of(yb)).all()
+
+
+def test_ln_width_768_matches_torch():
+    torch = pytest.importorskip("torch")
+    x = workloads.normal_rows(95, 300, 768, mean=0.25, std=3.0)
+    ref = torch.nn.functional.layer_norm(torch.from_numpy(x.astype(np.float64)), (768,), eps=1e-5)
+    assert np.array_equal(bits_of(oracle.layer_norm(x)), bits_of(ref.numpy().astype(np.float16)))
+
+
+@pytest.mark.parametrize("C", [192, 384, 768])
+def test_ln_affine_reduces_and_scales(C):
+    x = workloads.normal_rows(96, 200, C, mean=-1.0, std=2.0)
+    ones, zeros = np.ones(C, np.float16), np.zeros(C, np.float16)
+    # unit scale, zero shift: the plain LayerNorm
+    assert np.array_equal(bits_of(oracle.layer_norm_affine(x, ones, zeros)), bits_of(oracle.layer_norm(x)))
+    # a scale of 2 doubles every binary16 result exactly in the normal range (in
+    # the subnormal range the spacing is fixed at 2**-24, so doubling can round
+    # differently there)
+    twos = np.full(C, 2.0, np.float16)
+    y1 = oracle.layer_norm(x).astype(np.float64)
+    y2 = oracle.layer_norm_affine(x, twos, zeros).astype(np.float64)
+    normal = np.abs(y1) >= 2.0 ** -14
+    assert normal.mean() > 0.99
+    assert np.array_equal(y2[normal], 2.0 * y1[normal])
+    # zero scale leaves the shift
+    beta = workloads.normal_rows(97, 1, C)[0]
+    assert np.array_equal(bits_of(oracle.layer_norm_affine(x, zeros, beta)), bits_of(np.tile(beta, (200, 1))))
+
+
+@pytest.mark.parametrize("C", [192, 384, 768])
+def test_ln_affine_matches_torch(C):
+    torch = pytest.importorskip("torch")
+    x = workloads.normal_rows(98, 300, C)
+    g = workloads.normal_rows(99, 1, C, mean=1.0, std=0.2)[0]
+    b = workloads.normal_rows(100, 1, C, std=0.1)[0]
+    ref = torch.nn.functional.layer_norm(torch.from_numpy(x.astype(np.float64)), (C,),
+                                         weight=torch.from_numpy(g.astype(np.float64)),
+                                         bias=torch.from_numpy(b.astype(np.float64)), eps=1e-5)
+    assert np.array_equal(bits_of(oracle.layer_norm_affine(x, g, b)), bits_of(ref.numpy().astype(np.float16)))
+
+
+def test_ln_affine_two_valued_closed_form():
+    C, k, a, b = 192, 10, 0.5, -2.0
+    row = np.array([a] * k + [b] * (C - k), dtype=np.float16)[None, :]
+    g = np.full(C, 1.5, np.float16)
+    be = np.full(C, 0.25, np.float16)
+    getcontext().prec = 60
+    D = Decimal(a) - Decimal(b)
+    den = (Decimal(k) * Decimal(C - k) * D * D / Decimal(C * C) + Decimal(1e-5)).sqrt()
+    ya = Decimal(C - k) * D / Decimal(C) / den * Decimal(1.5) + Decimal(0.25)
+    yb = -Decimal(k) * D / Decimal(C) / den * Decimal(1.5) + Decimal(0.25)
+    y = oracle.layer_norm_affine(row, g, be)
+    assert (bits_of(y[0, :k]) == bits_of(np.float16(float(ya)))).all()
+    assert (bits_of(y[0, k:]) == bits_of(np.float16(float(yb)))).all()
+    r, y2 = oracle.add_ln_affine(np.zeros_like(row), row, g, be)
+    assert np.array_equal(bits_of(r), bits_of(row)) and np.array_equal(bits_of(y2), bits_of(y))
