@@ -21,9 +21,11 @@
  *    means nothing was enqueued; lwg_last_error() then describes the problem.
  *  - rows == 0 (or n_out == 0) returns LWG_OK without launching anything; the
  *    pointers are not inspected in that case.
- *  - Only C = 192 and C = 384 are served (section 3 of the BW1000 page: the
- *    model's widths are 192 and 384; other widths are refused, not served by an
- *    untested path). Other widths return LWG_ERR_UNSUPPORTED_WIDTH.
+ *  - C = 192 and C = 384 (the model's hidden widths, section 3 of the BW1000
+ *    page) and C = 768 (its patch-merge width: four 192-channel tokens
+ *    concatenated) are served, each with its own tests. The page refuses widths
+ *    without tests rather than serving them by an untested path; any other
+ *    width returns LWG_ERR_UNSUPPORTED_WIDTH.
  *  - Statistics (row mean and biased variance) are accumulated in binary64 from
  *    the binary16 inputs and each output is rounded once to binary16, to
  *    nearest-even. LayerNorm has no scale or shift: the BW1000 page folds the
@@ -44,7 +46,7 @@ extern "C" {
 typedef enum lwg_status {
     LWG_OK = 0,
     LWG_ERR_INVALID_ARGUMENT = 1,  /* null pointer, negative size, bad eps, bad window */
-    LWG_ERR_UNSUPPORTED_WIDTH = 2, /* C not in {192, 384} */
+    LWG_ERR_UNSUPPORTED_WIDTH = 2, /* C not in {192, 384, 768} */
     LWG_ERR_MISALIGNED = 3,        /* a tensor pointer not 16-byte aligned */
     LWG_ERR_ALIASING = 4,          /* an output overlaps an input in a way the call forbids */
     LWG_ERR_SIZE_MISMATCH = 5,     /* table length differs from the window token count */
@@ -175,6 +177,27 @@ int32_t lwg_window_reverse_add_ln(const void* win, int64_t n_win, const int32_t*
 int32_t lwg_add_norm_gather(const void* branch, const void* residual, void* residual_out,
                             int64_t n_src, int32_t C, const int32_t* table, int64_t n_out,
                             double eps, void* out, void* stream);
+
+/*
+ * Affine LayerNorm, for callers that do not fold the scale and shift into the
+ * next Linear (the BW1000 page, section 3, folds them at load time):
+ *   y[r, c] = (x[r, c] - mean_r) / sqrt(var_r + eps) * gamma[c] + beta[c]
+ * evaluated in binary64 and rounded once to binary16.
+ * gamma, beta : device binary16 [C], 16-byte aligned, read by every wave.
+ * x, y        : as in lwg_ln_fixed (y may equal x); y must not overlap gamma or beta.
+ */
+int32_t lwg_ln_affine(const void* x, const void* gamma, const void* beta, void* y,
+                      int64_t rows, int32_t C, double eps, void* stream);
+
+/*
+ * Residual add + affine LayerNorm: residual_out = FP16(residual + branch) as in
+ * lwg_add_ln (section 4), y = affine LayerNorm of residual_out as in
+ * lwg_ln_affine. Aliasing rules of lwg_add_ln; outputs must not overlap gamma
+ * or beta.
+ */
+int32_t lwg_add_ln_affine(const void* branch, const void* residual, const void* gamma,
+                          const void* beta, void* residual_out, void* y, int64_t rows,
+                          int32_t C, double eps, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* lwg_status_string(int32_t status);

@@ -23,6 +23,10 @@ and the window reverse that follows attention, plus the two fusions around it:
   window_reverse(rows, inverse)      rows back to token order (a gather by inverse)
   window_reverse_add_ln(rows, inverse, residual)  reverse + add + LayerNorm
   add_norm_gather(branch, residual, table)        add + LayerNorm + gather
+
+and, for callers that keep the LayerNorm scale and shift:
+  ln_affine(x, gamma, beta), add_ln_affine(branch, residual, gamma, beta)
+Widths: 192 and 384 (the model's), 768 (its patch-merge width).
 """
 from __future__ import annotations
 
@@ -33,12 +37,12 @@ import torch
 from . import _lib
 from ._lib import LwgError
 
-__all__ = ["ln_fixed", "add_ln", "window_token_count", "window_index_build", "window_table",
+__all__ = ["ln_fixed", "add_ln", "ln_affine", "add_ln_affine", "window_token_count", "window_index_build", "window_table",
            "window_gather", "norm_gather", "window_inverse_build", "window_inverse_table",
            "window_reverse", "window_reverse_add_ln", "add_norm_gather", "LwgError", "WIDTHS", "EPS",
            "library"]
 
-WIDTHS = (192, 384)
+WIDTHS = (192, 384, 768)
 EPS = 1e-5
 
 
@@ -62,7 +66,7 @@ def _rows(t: torch.Tensor, name: str) -> int:
     if t.dtype != torch.float16:
         raise RuntimeError(f"{name} must be float16, got {t.dtype}")
     if t.dim() < 1 or t.shape[-1] not in WIDTHS:
-        raise RuntimeError(f"{name} must have last dimension 192 or 384, got shape {tuple(t.shape)}")
+        raise RuntimeError(f"{name} must have last dimension 192, 384 or 768, got shape {tuple(t.shape)}")
     if not t.is_contiguous():
         raise RuntimeError(f"{name} must be contiguous")
     if t.device.type != "cuda":
@@ -112,6 +116,45 @@ def add_ln(branch: torch.Tensor, residual: torch.Tensor, eps: float = EPS,
     with torch.cuda.device(residual.device):
         _lib.check(lib.lwg_add_ln(_ptr(branch), _ptr(residual), _ptr(r), _ptr(y), rows,
                                   residual.shape[-1], float(eps), _stream(residual.device)))
+    return r, y
+
+
+def _affine_params(gamma, beta, C, device):
+    for name, t in (("gamma", gamma), ("beta", beta)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float16 or t.dim() != 1 or t.numel() != C:
+            raise RuntimeError(f"{name} must be a 1-D float16 tensor of length {C}")
+        if not t.is_contiguous() or t.device != device:
+            raise RuntimeError(f"{name} must be contiguous and on {device}")
+
+
+def ln_affine(x: torch.Tensor, gamma: torch.Tensor, beta: torch.Tensor, eps: float = EPS,
+              out: torch.Tensor = None) -> torch.Tensor:
+    """LayerNorm over the last dimension with a per-channel scale and shift."""
+    rows = _rows(x, "x")
+    _affine_params(gamma, beta, x.shape[-1], x.device)
+    y = _out_like(out, x.shape, x.device, "out")
+    lib = _lib.load()
+    with torch.cuda.device(x.device):
+        _lib.check(lib.lwg_ln_affine(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), rows, x.shape[-1], float(eps),
+                                     _stream(x.device)))
+    return y
+
+
+def add_ln_affine(branch: torch.Tensor, residual: torch.Tensor, gamma: torch.Tensor, beta: torch.Tensor,
+                  eps: float = EPS, residual_out: torch.Tensor = None, out: torch.Tensor = None):
+    """Returns (FP16(residual + branch), affine LayerNorm of it)."""
+    rows = _rows(residual, "residual")
+    _rows(branch, "branch")
+    if tuple(branch.shape) != tuple(residual.shape):
+        raise RuntimeError(f"branch shape {tuple(branch.shape)} != residual shape {tuple(residual.shape)}")
+    _same_device(residual, ("branch", branch))
+    _affine_params(gamma, beta, residual.shape[-1], residual.device)
+    r = _out_like(residual_out, residual.shape, residual.device, "residual_out")
+    y = _out_like(out, residual.shape, residual.device, "out")
+    lib = _lib.load()
+    with torch.cuda.device(residual.device):
+        _lib.check(lib.lwg_add_ln_affine(_ptr(branch), _ptr(residual), _ptr(gamma), _ptr(beta), _ptr(r), _ptr(y),
+                                         rows, residual.shape[-1], float(eps), _stream(residual.device)))
     return r, y
 
 
@@ -319,7 +362,9 @@ def prepare(op: str, *tensors, eps: float = EPS, grid=None, window=None, shift=(
       prepare("norm_gather", x, table, out)
       prepare("window_inverse_build", inverse, grid=..., window=..., shift=...)
       prepare("window_reverse_add_ln", rows, inverse, residual, residual_out, y)
-      prepare("add_norm_gather", branch, residual, residual_out, table, out)"""
+      prepare("add_norm_gather", branch, residual, residual_out, table, out)
+      prepare("ln_affine", x, gamma, beta, y)
+      prepare("add_ln_affine", branch, residual, gamma, beta, residual_out, y)"""
     lib = _lib.load()
     if op == "ln_fixed":
         x, y = tensors
@@ -382,6 +427,24 @@ def prepare(op: str, *tensors, eps: float = EPS, grid=None, window=None, shift=(
         dev = r.device
         fn, args = lib.lwg_add_norm_gather, (_ptr(b), _ptr(r), _ptr(ro), n_src, r.shape[-1], _ptr(table),
                                              table.numel(), float(eps), _ptr(out), _stream(dev))
+    elif op == "ln_affine":
+        x, g, b, y = tensors
+        rows = _rows(x, "x")
+        _affine_params(g, b, x.shape[-1], x.device)
+        _out_like(y, x.shape, x.device, "y")
+        dev = x.device
+        fn, args = lib.lwg_ln_affine, (_ptr(x), _ptr(g), _ptr(b), _ptr(y), rows, x.shape[-1], float(eps),
+                                       _stream(dev))
+    elif op == "add_ln_affine":
+        br, r, g, b, ro, y = tensors
+        rows = _rows(r, "residual")
+        _rows(br, "branch")
+        _affine_params(g, b, r.shape[-1], r.device)
+        _out_like(ro, r.shape, r.device, "residual_out")
+        _out_like(y, r.shape, r.device, "y")
+        dev = r.device
+        fn, args = lib.lwg_add_ln_affine, (_ptr(br), _ptr(r), _ptr(g), _ptr(b), _ptr(ro), _ptr(y), rows,
+                                           r.shape[-1], float(eps), _stream(dev))
     else:
         raise ValueError(f"unknown op {op!r}")
     return Prepared(fn, args, tensors)

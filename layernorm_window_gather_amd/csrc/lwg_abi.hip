@@ -56,8 +56,8 @@ bool same_or_disjoint(const void* a, const void* b, uint64_t n) {
 }
 
 int32_t check_width(const char* fn, int32_t C) {
-    if (C != 192 && C != 384)
-        return fail(LWG_ERR_UNSUPPORTED_WIDTH, "%s: C=%d is not served (only 192 and 384)", fn, C);
+    if (C != 192 && C != 384 && C != 768)
+        return fail(LWG_ERR_UNSUPPORTED_WIDTH, "%s: C=%d is not served (only 192, 384 and 768)", fn, C);
     return LWG_OK;
 }
 
@@ -339,5 +339,51 @@ LWG_EXPORT int32_t lwg_add_norm_gather(const void* branch, const void* residual,
     }
     return hip_result(lwg::launch_add_norm_gather(branch, residual, residual_out, n_src, C, table, n_out, eps,
                                                   out, static_cast<hipStream_t>(stream)),
+                      fn);
+}
+
+LWG_EXPORT int32_t lwg_ln_affine(const void* x, const void* gamma, const void* beta, void* y, int64_t rows,
+                                 int32_t C, double eps, void* stream) {
+    static const char* fn = "lwg_ln_affine";
+    int32_t st;
+    if ((st = check_width(fn, C)) || (st = check_eps(fn, eps)) || (st = check_rows(fn, "rows", rows)))
+        return st;
+    if (rows == 0) return ok();
+    if ((st = check_tensor(fn, "x", x)) || (st = check_tensor(fn, "gamma", gamma)) ||
+        (st = check_tensor(fn, "beta", beta)) || (st = check_tensor(fn, "y", y)))
+        return st;
+    const uint64_t bytes = static_cast<uint64_t>(rows) * C * 2;
+    if (!same_or_disjoint(x, y, bytes))
+        return fail(LWG_ERR_ALIASING, "%s: y partially overlaps x (only y == x is allowed)", fn);
+    if (overlap(y, bytes, gamma, static_cast<uint64_t>(C) * 2) || overlap(y, bytes, beta, static_cast<uint64_t>(C) * 2))
+        return fail(LWG_ERR_ALIASING, "%s: y overlaps gamma or beta", fn);
+    return hip_result(lwg::launch_ln_affine(x, gamma, beta, y, rows, C, eps, static_cast<hipStream_t>(stream)), fn);
+}
+
+LWG_EXPORT int32_t lwg_add_ln_affine(const void* branch, const void* residual, const void* gamma,
+                                     const void* beta, void* residual_out, void* y, int64_t rows, int32_t C,
+                                     double eps, void* stream) {
+    static const char* fn = "lwg_add_ln_affine";
+    int32_t st;
+    if ((st = check_width(fn, C)) || (st = check_eps(fn, eps)) || (st = check_rows(fn, "rows", rows)))
+        return st;
+    if (rows == 0) return ok();
+    if ((st = check_tensor(fn, "branch", branch)) || (st = check_tensor(fn, "residual", residual)) ||
+        (st = check_tensor(fn, "gamma", gamma)) || (st = check_tensor(fn, "beta", beta)) ||
+        (st = check_tensor(fn, "residual_out", residual_out)) || (st = check_tensor(fn, "y", y)))
+        return st;
+    const uint64_t bytes = static_cast<uint64_t>(rows) * C * 2;
+    const uint64_t pbytes = static_cast<uint64_t>(C) * 2;
+    if (overlap(y, bytes, residual_out, bytes))
+        return fail(LWG_ERR_ALIASING, "%s: y and residual_out overlap", fn);
+    if (!same_or_disjoint(residual_out, residual, bytes) || !same_or_disjoint(residual_out, branch, bytes) ||
+        !same_or_disjoint(y, residual, bytes) || !same_or_disjoint(y, branch, bytes))
+        return fail(LWG_ERR_ALIASING,
+                    "%s: an output partially overlaps an input (only exact in-place aliasing is allowed)", fn);
+    if (overlap(y, bytes, gamma, pbytes) || overlap(y, bytes, beta, pbytes) ||
+        overlap(residual_out, bytes, gamma, pbytes) || overlap(residual_out, bytes, beta, pbytes))
+        return fail(LWG_ERR_ALIASING, "%s: an output overlaps gamma or beta", fn);
+    return hip_result(lwg::launch_add_ln_affine(branch, residual, gamma, beta, residual_out, y, rows, C, eps,
+                                                static_cast<hipStream_t>(stream)),
                       fn);
 }

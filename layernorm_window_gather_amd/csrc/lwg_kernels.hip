@@ -26,6 +26,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "lwg_launch.h"
 
 namespace lwg {
@@ -165,16 +167,14 @@ __device__ __forceinline__ double rsqrt_refined(double a) {
     return __builtin_fma(r, __builtin_fma(-h, r, 0.5), r);
 }
 
-// LayerNorm of the row whose 1/LPR share this lane holds in v (section 3):
-// mean, biased variance of the deviations (two passes over registers), then
-// (x - mean) / sqrt(var + eps) rounded to binary16, written back into v.
-// Every kernel that normalises a row calls this same function with the same
-// (C, K), so their outputs agree bit for bit.
+// Row statistics of LayerNorm (section 3) for the row whose 1/LPR share this
+// lane holds in v: the mean and the biased variance of the deviations, in two
+// passes over registers. On return x holds this lane's deviations from the mean
+// and the result is 1/sqrt(var + eps).
 template <int C, int K>
-__device__ __forceinline__ void layer_norm_lane(chunk_t (&v)[K], double eps) {
+__device__ __forceinline__ double row_stats(const chunk_t (&v)[K], double (&x)[8 * K], double eps) {
     using T = Tile<C, K>;
     constexpr double kInvC = 1.0 / C;
-    double x[T::kValues];
 #pragma unroll
     for (int k = 0; k < K; ++k) unpack8(v[k], x + 8 * k);
 
@@ -186,7 +186,6 @@ __device__ __forceinline__ void layer_norm_lane(chunk_t (&v)[K], double eps) {
     }
     const double mean = group_sum<T::kLanes>(s0 + s1) * kInvC;
 
-    // x becomes the deviation from the mean; its squares give the variance
     double q0 = 0.0, q1 = 0.0;
 #pragma unroll
     for (int i = 0; i < T::kValues; i += 2) {
@@ -195,13 +194,45 @@ __device__ __forceinline__ void layer_norm_lane(chunk_t (&v)[K], double eps) {
         q0 = __builtin_fma(x[i], x[i], q0);
         q1 = __builtin_fma(x[i + 1], x[i + 1], q1);
     }
-    const double rstd = rsqrt_refined(group_sum<T::kLanes>(q0 + q1) * kInvC + eps);
+    return rsqrt_refined(group_sum<T::kLanes>(q0 + q1) * kInvC + eps);
+}
 
+// LayerNorm of the row whose 1/LPR share this lane holds in v: (x - mean) /
+// sqrt(var + eps) rounded to binary16, written back into v. Every kernel that
+// normalises a row calls this same function with the same (C, K), so their
+// outputs agree bit for bit.
+template <int C, int K>
+__device__ __forceinline__ void layer_norm_lane(chunk_t (&v)[K], double eps) {
+    double x[8 * K];
+    const double rstd = row_stats<C, K>(v, x, eps);
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         const double* xk = x + 8 * k;
         v[k] = chunk_t{pack2(xk[0] * rstd, xk[1] * rstd), pack2(xk[2] * rstd, xk[3] * rstd),
                        pack2(xk[4] * rstd, xk[5] * rstd), pack2(xk[6] * rstd, xk[7] * rstd)};
+    }
+}
+
+// Affine LayerNorm: ((x - mean) / sqrt(var + eps)) * gamma + beta in binary64,
+// rounded once to binary16. gamma and beta are binary16 [C]; this lane reads its
+// columns chunk by chunk as it writes them (small arrays that stay in cache), so
+// only one chunk of them is live next to the row's deviations.
+template <int C, int K>
+__device__ __forceinline__ void layer_norm_affine_lane(chunk_t (&v)[K], const chunk_t* gamma,
+                                                       const chunk_t* beta, int sub, double eps) {
+    using T = Tile<C, K>;
+    double x[8 * K];
+    const double rstd = row_stats<C, K>(v, x, eps);
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        double gk[8], bk[8];
+        unpack8(gamma[sub + k * T::kLanes], gk);
+        unpack8(beta[sub + k * T::kLanes], bk);
+        const double* xk = x + 8 * k;
+        v[k] = chunk_t{pack2(__builtin_fma(xk[0] * rstd, gk[0], bk[0]), __builtin_fma(xk[1] * rstd, gk[1], bk[1])),
+                       pack2(__builtin_fma(xk[2] * rstd, gk[2], bk[2]), __builtin_fma(xk[3] * rstd, gk[3], bk[3])),
+                       pack2(__builtin_fma(xk[4] * rstd, gk[4], bk[4]), __builtin_fma(xk[5] * rstd, gk[5], bk[5])),
+                       pack2(__builtin_fma(xk[6] * rstd, gk[6], bk[6]), __builtin_fma(xk[7] * rstd, gk[7], bk[7]))};
     }
 }
 
@@ -282,6 +313,70 @@ __global__ __launch_bounds__(kBlock) void add_ln_kernel(const chunk_t* branch, c
             for (int k = 0; k < K; ++k) store16<H>(residual_out + base + k * T::kLanes, r[k]);
         }
         layer_norm_lane<C, K>(r, eps);
+        if (live) {
+#pragma unroll
+            for (int k = 0; k < K; ++k) store16<H>(y + base + k * T::kLanes, r[k]);
+        }
+    }
+}
+
+// Affine LayerNorm and residual add + affine LayerNorm. gamma and beta are
+// binary16 [C], read through the caches by every wave (2*C*2 bytes, not HBM
+// traffic after the first waves). y may alias x, and residual_out / y may alias
+// the inputs as in the plain kernels.
+template <int C, int K, class H>
+__global__ __launch_bounds__(kBlock) void ln_affine_kernel(const chunk_t* x, const chunk_t* gamma,
+                                                           const chunk_t* beta, chunk_t* y,
+                                                           int64_t rows, double eps) {
+    using T = Tile<C, K>;
+    const int lane = threadIdx.x & 63;
+    const int sub = lane % T::kLanes;
+    for (int64_t w = first_wave<T>(); w * T::kRowsPerWave < rows; w += wave_stride()) {
+        const int64_t row = w * T::kRowsPerWave + lane / T::kLanes;
+        const bool live = row < rows;
+        const int64_t base = row * T::kChunks + sub;
+        chunk_t v[K];
+        zero(v);
+        if (live) {
+#pragma unroll
+            for (int k = 0; k < K; ++k) v[k] = load16<H>(x + base + k * T::kLanes);
+        }
+        layer_norm_affine_lane<C, K>(v, gamma, beta, sub, eps);
+        if (live) {
+#pragma unroll
+            for (int k = 0; k < K; ++k) store16<H>(y + base + k * T::kLanes, v[k]);
+        }
+    }
+}
+
+template <int C, int K, class H>
+__global__ __launch_bounds__(kBlock) void add_ln_affine_kernel(const chunk_t* branch, const chunk_t* residual,
+                                                               const chunk_t* gamma, const chunk_t* beta,
+                                                               chunk_t* residual_out, chunk_t* y,
+                                                               int64_t rows, double eps) {
+    using T = Tile<C, K>;
+    const int lane = threadIdx.x & 63;
+    const int sub = lane % T::kLanes;
+    for (int64_t w = first_wave<T>(); w * T::kRowsPerWave < rows; w += wave_stride()) {
+        const int64_t row = w * T::kRowsPerWave + lane / T::kLanes;
+        const bool live = row < rows;
+        const int64_t base = row * T::kChunks + sub;
+        chunk_t b[K], r[K];
+        zero(b);
+        zero(r);
+        if (live) {
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                b[k] = load16<H>(branch + base + k * T::kLanes);
+                r[k] = load16<H>(residual + base + k * T::kLanes);
+            }
+        }
+        residual_add<K>(b, r);
+        if (live) {
+#pragma unroll
+            for (int k = 0; k < K; ++k) store16<H>(residual_out + base + k * T::kLanes, r[k]);
+        }
+        layer_norm_affine_lane<C, K>(r, gamma, beta, sub, eps);
         if (live) {
 #pragma unroll
             for (int k = 0; k < K; ++k) store16<H>(y + base + k * T::kLanes, r[k]);
@@ -473,23 +568,27 @@ __global__ __launch_bounds__(kBlock) void window_inverse_kernel(WindowGeometry g
 // K (chunks per lane) is fixed per width, so that every LayerNorm kernel of one
 // width reduces a row in the same order and their outputs agree bit for bit:
 // K = 3 at C = 192 and K = 6 at C = 384, i.e. 8 lanes per row, each wave
-// instruction reading whole 128-byte lines of 8 rows. (4 lanes per row, 64-byte
+// instruction reading whole 128-byte lines of 8 rows; K = 6 at C = 768. (4 lanes per row, 64-byte
 // pieces of a line per instruction, measured 10-20% slower.)
 // Every kernel streams its inputs once and never re-reads its outputs, so all
 // loads and stores carry the non-temporal hint; on cold data that beat plain
 // and store-only-hinted accesses for every kernel. The grid is one tile per
 // wave, except the C = 384 norm-gather, which is capped at 4 workgroups per
 // compute unit with each wave looping over tiles.
-enum class Op { kLn, kAddLn, kGather, kNormGather, kReverseAddLn, kAddNormGather };
+enum class Op { kLn, kAddLn, kGather, kNormGather, kReverseAddLn, kAddNormGather, kLnAffine, kAddLnAffine };
 
 template <int C> struct Width;
 template <> struct Width<192> { static constexpr int K = 3; };
 template <> struct Width<384> { static constexpr int K = 6; };
+// the patch-merge width: 16 lanes per row, 6 chunks each (whole 256-byte pieces
+// of 4 rows per wave instruction)
+template <> struct Width<768> { static constexpr int K = 6; };
 
 using Streaming = Hints<true, true>;
 
 template <int C, Op O> struct Launch { using H = Streaming; static constexpr int kBlocksPerCu = 0; };
 template <> struct Launch<384, Op::kNormGather> { using H = Streaming; static constexpr int kBlocksPerCu = 4; };
+
 
 int g_cus = 0;  // compute units of the current device, read once
 
@@ -544,16 +643,25 @@ hipError_t gather_c(const void* x, int64_t n_src, const int32_t* table, int64_t 
 
 }  // namespace
 
+// Runs f(std::integral_constant<int, C>) for the served width C (192, 384 or
+// 768; the C ABI has already refused any other).
+template <class F>
+hipError_t by_width(int32_t C, F&& f) {
+    switch (C) {
+        case 192: return f(std::integral_constant<int, 192>{});
+        case 384: return f(std::integral_constant<int, 384>{});
+        default: return f(std::integral_constant<int, 768>{});
+    }
+}
+
 hipError_t launch_ln_fixed(const void* x, void* y, int64_t rows, int32_t C, double eps,
                            hipStream_t stream) {
-    return C == 192 ? ln_fixed_c<192>(x, y, rows, eps, stream)
-                    : ln_fixed_c<384>(x, y, rows, eps, stream);
+    return by_width(C, [&](auto c) { return ln_fixed_c<decltype(c)::value>(x, y, rows, eps, stream); });
 }
 
 hipError_t launch_add_ln(const void* branch, const void* residual, void* residual_out, void* y,
                          int64_t rows, int32_t C, double eps, hipStream_t stream) {
-    return C == 192 ? add_ln_c<192>(branch, residual, residual_out, y, rows, eps, stream)
-                    : add_ln_c<384>(branch, residual, residual_out, y, rows, eps, stream);
+    return by_width(C, [&](auto c) { return add_ln_c<decltype(c)::value>(branch, residual, residual_out, y, rows, eps, stream); });
 }
 
 hipError_t launch_window_index(const WindowGeometry& g, int32_t* table, hipStream_t stream) {
@@ -564,14 +672,12 @@ hipError_t launch_window_index(const WindowGeometry& g, int32_t* table, hipStrea
 
 hipError_t launch_window_gather(const void* x, int64_t n_src, int32_t C, const int32_t* table,
                                 int64_t n_out, void* out, hipStream_t stream) {
-    return C == 192 ? gather_c<192, false>(x, n_src, table, n_out, 0.0, out, stream)
-                    : gather_c<384, false>(x, n_src, table, n_out, 0.0, out, stream);
+    return by_width(C, [&](auto c) { return gather_c<decltype(c)::value, false>(x, n_src, table, n_out, 0.0, out, stream); });
 }
 
 hipError_t launch_norm_gather(const void* x, int64_t n_src, int32_t C, const int32_t* table,
                               int64_t n_out, double eps, void* out, hipStream_t stream) {
-    return C == 192 ? gather_c<192, true>(x, n_src, table, n_out, eps, out, stream)
-                    : gather_c<384, true>(x, n_src, table, n_out, eps, out, stream);
+    return by_width(C, [&](auto c) { return gather_c<decltype(c)::value, true>(x, n_src, table, n_out, eps, out, stream); });
 }
 
 hipError_t launch_window_inverse(const WindowGeometry& g, int32_t* inverse, hipStream_t stream) {
@@ -595,8 +701,7 @@ hipError_t reverse_add_ln_c(const void* win, int64_t n_win, const int32_t* idx, 
 hipError_t launch_reverse_add_ln(const void* win, int64_t n_win, const int32_t* inverse,
                                  const void* residual, void* residual_out, void* y, int64_t rows,
                                  int32_t C, double eps, hipStream_t stream) {
-    return C == 192 ? reverse_add_ln_c<192>(win, n_win, inverse, residual, residual_out, y, rows, eps, stream)
-                    : reverse_add_ln_c<384>(win, n_win, inverse, residual, residual_out, y, rows, eps, stream);
+    return by_width(C, [&](auto c) { return reverse_add_ln_c<decltype(c)::value>(win, n_win, inverse, residual, residual_out, y, rows, eps, stream); });
 }
 
 template <int C>
@@ -613,8 +718,42 @@ hipError_t add_norm_gather_c(const void* b, const void* r, void* ro, int64_t n_s
 hipError_t launch_add_norm_gather(const void* branch, const void* residual, void* residual_out,
                                   int64_t n_src, int32_t C, const int32_t* table, int64_t n_out,
                                   double eps, void* out, hipStream_t stream) {
-    return C == 192 ? add_norm_gather_c<192>(branch, residual, residual_out, n_src, table, n_out, eps, out, stream)
-                    : add_norm_gather_c<384>(branch, residual, residual_out, n_src, table, n_out, eps, out, stream);
+    return by_width(C, [&](auto c) { return add_norm_gather_c<decltype(c)::value>(branch, residual, residual_out, n_src, table, n_out, eps, out, stream); });
+}
+
+template <int C>
+hipError_t ln_affine_c(const void* x, const void* g, const void* b, void* y, int64_t rows, double eps,
+                       hipStream_t s) {
+    using L = Launch<C, Op::kLnAffine>;
+    ln_affine_kernel<C, Width<C>::K, typename L::H><<<grid_for<C, Op::kLnAffine>(rows), kBlock, 0, s>>>(
+        static_cast<const chunk_t*>(x), static_cast<const chunk_t*>(g), static_cast<const chunk_t*>(b),
+        static_cast<chunk_t*>(y), rows, eps);
+    return hipGetLastError();
+}
+
+hipError_t launch_ln_affine(const void* x, const void* gamma, const void* beta, void* y, int64_t rows,
+                            int32_t C, double eps, hipStream_t stream) {
+    return by_width(C, [&](auto c) { return ln_affine_c<decltype(c)::value>(x, gamma, beta, y, rows, eps, stream); });
+}
+
+template <int C>
+hipError_t add_ln_affine_c(const void* br, const void* r, const void* g, const void* b, void* ro, void* y,
+                           int64_t rows, double eps, hipStream_t s) {
+    using L = Launch<C, Op::kAddLnAffine>;
+    add_ln_affine_kernel<C, Width<C>::K, typename L::H>
+        <<<grid_for<C, Op::kAddLnAffine>(rows), kBlock, 0, s>>>(
+            static_cast<const chunk_t*>(br), static_cast<const chunk_t*>(r), static_cast<const chunk_t*>(g),
+            static_cast<const chunk_t*>(b), static_cast<chunk_t*>(ro), static_cast<chunk_t*>(y), rows, eps);
+    return hipGetLastError();
+}
+
+hipError_t launch_add_ln_affine(const void* branch, const void* residual, const void* gamma, const void* beta,
+                                void* residual_out, void* y, int64_t rows, int32_t C, double eps,
+                                hipStream_t stream) {
+    return by_width(C, [&](auto c) {
+        return add_ln_affine_c<decltype(c)::value>(branch, residual, gamma, beta, residual_out, y, rows, eps,
+                                                   stream);
+    });
 }
 
 }  // namespace lwg

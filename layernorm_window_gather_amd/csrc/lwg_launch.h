@@ -1,6 +1,6 @@
 // Internal launchers between the C ABI (argument checks) and the kernels.
 // Every launcher assumes its arguments were validated by the caller: sizes in
-// range, C in {192, 384}, pointers non-null and 16-byte aligned.
+// range, C in {192, 384, 768}, pointers non-null and 16-byte aligned.
 #ifndef LWG_LAUNCH_H
 #define LWG_LAUNCH_H
 
@@ -51,6 +51,11 @@ hipError_t launch_window_gather(const void* x, int64_t n_src, int32_t C, const i
 hipError_t launch_norm_gather(const void* x, int64_t n_src, int32_t C, const int32_t* table,
                               int64_t n_out, double eps, void* out, hipStream_t stream);
 hipError_t launch_window_inverse(const WindowGeometry& g, int32_t* inverse, hipStream_t stream);
+hipError_t launch_ln_affine(const void* x, const void* gamma, const void* beta, void* y, int64_t rows,
+                            int32_t C, double eps, hipStream_t stream);
+hipError_t launch_add_ln_affine(const void* branch, const void* residual, const void* gamma, const void* beta,
+                                void* residual_out, void* y, int64_t rows, int32_t C, double eps,
+                                hipStream_t stream);
 hipError_t launch_reverse_add_ln(const void* win, int64_t n_win, const int32_t* inverse,
                                  const void* residual, void* residual_out, void* y, int64_t rows,
                                  int32_t C, double eps, hipStream_t stream);

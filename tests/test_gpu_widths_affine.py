@@ -1,0 +1,111 @@
+"""Parity of the patch-merge width (C = 768) in every kernel, and of the affine
+LayerNorm calls, with the CPU oracle."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from workloads import PATCH_MERGE, WINDOW, SHIFT, NO_SHIFT
+
+from parity_helpers import assert_bit_exact, assert_ln_close, bits, host, to_dev
+
+torch = pytest.importorskip("torch")
+lwg = pytest.importorskip("layernorm_window_gather_amd")
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("rows", [1, 3, 4, 5, 63, 64, 65, 1000, 4097])
+def test_width_768_ln_and_add_ln_ragged(dev, rows):
+    x = workloads.normal_rows(300 + rows, rows, 768, mean=0.2, std=1.5)
+    res = workloads.normal_rows(400 + rows, rows, 768)
+    assert_ln_close(host(lwg.ln_fixed(to_dev(x, dev))), oracle.layer_norm(x), f"ln 768 rows={rows}")
+    r, y = lwg.add_ln(to_dev(x, dev), to_dev(res, dev))
+    r_ref, y_ref = oracle.add_ln(x, res)
+    assert_bit_exact(host(r), r_ref, f"residual 768 rows={rows}")
+    assert_ln_close(host(y), y_ref, f"add_ln 768 rows={rows}")
+
+
+def test_width_768_patch_merge_shape(dev):
+    n = PATCH_MERGE.tokens
+    nc, off = workloads.stress_row_classes(11, n)
+    x = workloads.mixed_rows(12, n, 768, nc, off)
+    tx = to_dev(x, dev)
+    y = host(lwg.ln_fixed(tx))
+    assert_ln_close(y, oracle.layer_norm(x), "patch-merge LayerNorm [32760, 768]")
+    y2 = host(lwg.ln_fixed(tx, out=tx))
+    assert_bit_exact(y2, y, "in place")
+
+
+@pytest.mark.parametrize("grid,shift", [((2, 12, 24), SHIFT), ((3, 7, 13), NO_SHIFT), ((4, 9, 26), (3, 13, 30))])
+def test_width_768_gathers_and_fusions(dev, grid, shift):
+    n = int(np.prod(grid))
+    x = workloads.normal_rows(13, n, 768)
+    br = workloads.normal_rows(14, n, 768)
+    table = oracle.window_index_table(grid, WINDOW, shift)
+    t = lwg.window_index_build(grid, WINDOW, shift, device=dev)
+    inv = lwg.window_inverse_build(grid, WINDOW, shift, device=dev)
+    tx = to_dev(x, dev)
+    assert_bit_exact(host(lwg.window_gather(tx, t)), oracle.window_gather(x, table), "gather 768")
+    ng = host(lwg.norm_gather(tx, t))
+    assert_ln_close(ng, oracle.norm_gather(x, table), "norm_gather 768")
+    assert_bit_exact(ng, host(lwg.window_gather(lwg.ln_fixed(tx), t)), "norm_gather == gather(ln) 768")
+    rows = workloads.normal_rows(15, table.size, 768)
+    r, y = lwg.window_reverse_add_ln(to_dev(rows, dev), inv, tx)
+    r_ref, y_ref = oracle.window_reverse_add_ln(rows, x, grid, WINDOW, shift)
+    assert_bit_exact(host(r), r_ref, "reverse_add_ln residual 768")
+    assert_ln_close(host(y), y_ref, "reverse_add_ln 768")
+    r2, g = lwg.add_norm_gather(to_dev(br, dev), tx, t)
+    r2_ref, g_ref = oracle.add_norm_gather(br, x, table)
+    assert_bit_exact(host(r2), r2_ref, "add_norm_gather residual 768")
+    assert_ln_close(host(g), g_ref, "add_norm_gather 768")
+
+
+def _params(C, seed):
+    g = workloads.normal_rows(seed, 1, C, mean=1.0, std=0.3)[0]
+    b = workloads.normal_rows(seed + 1, 1, C, std=0.5)[0]
+    return g, b
+
+
+@pytest.mark.parametrize("C", [192, 384, 768])
+@pytest.mark.parametrize("rows", [1, 7, 65, 2049])
+def test_ln_affine_parity(dev, C, rows):
+    x = workloads.normal_rows(500 + rows, rows, C, mean=-0.7, std=2.0)
+    g, b = _params(C, 17)
+    y = host(lwg.ln_affine(to_dev(x, dev), to_dev(g, dev), to_dev(b, dev)))
+    assert_ln_close(y, oracle.layer_norm_affine(x, g, b), f"ln_affine C={C} rows={rows}")
+
+
+@pytest.mark.parametrize("C", [192, 384, 768])
+def test_ln_affine_identity_params_equal_ln_fixed(dev, C):
+    x = workloads.normal_rows(21, 3000, C)
+    tx = to_dev(x, dev)
+    one = torch.ones(C, dtype=torch.float16, device=dev)
+    zero = torch.zeros(C, dtype=torch.float16, device=dev)
+    assert_bit_exact(host(lwg.ln_affine(tx, one, zero)), host(lwg.ln_fixed(tx)), f"ln_affine(1,0) C={C}")
+
+
+@pytest.mark.parametrize("C", [192, 384, 768])
+def test_add_ln_affine_parity_and_aliasing(dev, C):
+    rows = 3001
+    nc, off = workloads.stress_row_classes(22, rows)
+    res = workloads.mixed_rows(23, rows, C, nc, off)
+    br = workloads.mixed_rows(24, rows, C, nc, off, offset_mean=0.0)
+    g, b = _params(C, 25)
+    tg, tb_ = to_dev(g, dev), to_dev(b, dev)
+    r_ref, y_ref = oracle.add_ln_affine(br, res, g, b)
+    r, y = lwg.add_ln_affine(to_dev(br, dev), to_dev(res, dev), tg, tb_)
+    assert_bit_exact(host(r), r_ref, f"add_ln_affine residual C={C}")
+    assert_ln_close(host(y), y_ref, f"add_ln_affine C={C}")
+    tbr, tr = to_dev(br, dev), to_dev(res, dev)
+    lwg.add_ln_affine(tbr, tr, tg, tb_, residual_out=tr, out=tbr)
+    assert_bit_exact(host(tr), r_ref, "in-place residual")
+    assert_ln_close(host(tbr), y_ref, "y over the branch")
+
+
+def test_affine_parameter_checks(dev):
+    x = torch.zeros(4, 192, dtype=torch.float16, device=dev)
+    with pytest.raises(RuntimeError, match="gamma"):
+        lwg.ln_affine(x, torch.ones(191, dtype=torch.float16, device=dev), torch.zeros(192, dtype=torch.float16, device=dev))
+    with pytest.raises(RuntimeError, match="beta"):
+        lwg.ln_affine(x, torch.ones(192, dtype=torch.float16, device=dev), torch.zeros(192, dtype=torch.float32, device=dev))

@@ -41,6 +41,9 @@ class Level:
 # Level 1: [1,131040,192] on an 8 x 182 x 90 grid; level 2: [1,32760,384] on 8 x 91 x 45.
 LEVEL1 = Level("level1", (8, 182, 90), 192)
 LEVEL2 = Level("level2", (8, 91, 45), 384)
+# Patch merging from level 1 to level 2 normalises 4 x 192 = 768 concatenated
+# channels of each merged token, on the level-2 grid.
+PATCH_MERGE = Level("patch_merge", (8, 91, 45), 768)
 # The tiny case: a 2 x 12 x 24 grid, exactly four (2,6,12) windows with no padding.
 TINY = Level("tiny", (2, 12, 24), 192)
 
