@@ -321,17 +321,34 @@ __global__ __launch_bounds__(kBlock) void add_ln_kernel(const chunk_t* branch, c
 }
 
 // Affine LayerNorm and residual add + affine LayerNorm. gamma and beta are
-// binary16 [C], read through the caches by every wave (2*C*2 bytes, not HBM
-// traffic after the first waves). y may alias x, and residual_out / y may alias
-// the inputs as in the plain kernels.
+// binary16 [C]; each workgroup copies them once into LDS (2*C*2 bytes, at most
+// 3 KB) and every lane reads its columns from there chunk by chunk, so the
+// parameters neither occupy the vector-memory path nor sit widened in
+// registers. y may alias x, and residual_out / y may alias the inputs as in the
+// plain kernels.
+template <int C>
+__device__ __forceinline__ void stage_params(chunk_t* params, const chunk_t* gamma, const chunk_t* beta) {
+    constexpr int kChunks = C / 8;
+    for (int i = threadIdx.x; i < 2 * kChunks; i += kBlock)
+        params[i] = i < kChunks ? gamma[i] : beta[i - kChunks];
+    __syncthreads();
+}
+
 template <int C, int K, class H>
 __global__ __launch_bounds__(kBlock) void ln_affine_kernel(const chunk_t* x, const chunk_t* gamma,
                                                            const chunk_t* beta, chunk_t* y,
                                                            int64_t rows, double eps) {
     using T = Tile<C, K>;
+    __shared__ chunk_t params[2 * T::kChunks];
+    stage_params<C>(params, gamma, beta);
+    gamma = params;
+    beta = params + T::kChunks;
     const int lane = threadIdx.x & 63;
     const int sub = lane % T::kLanes;
     for (int64_t w = first_wave<T>(); w * T::kRowsPerWave < rows; w += wave_stride()) {
+        // re-read gamma/beta from LDS per row tile instead of letting the
+        // compiler hoist 2*K widened chunks out of the loop into registers
+        asm volatile("" ::: "memory");
         const int64_t row = w * T::kRowsPerWave + lane / T::kLanes;
         const bool live = row < rows;
         const int64_t base = row * T::kChunks + sub;
@@ -355,9 +372,14 @@ __global__ __launch_bounds__(kBlock) void add_ln_affine_kernel(const chunk_t* br
                                                                chunk_t* residual_out, chunk_t* y,
                                                                int64_t rows, double eps) {
     using T = Tile<C, K>;
+    __shared__ chunk_t params[2 * T::kChunks];
+    stage_params<C>(params, gamma, beta);
+    gamma = params;
+    beta = params + T::kChunks;
     const int lane = threadIdx.x & 63;
     const int sub = lane % T::kLanes;
     for (int64_t w = first_wave<T>(); w * T::kRowsPerWave < rows; w += wave_stride()) {
+        asm volatile("" ::: "memory");  // as in ln_affine_kernel: no hoisting of gamma/beta
         const int64_t row = w * T::kRowsPerWave + lane / T::kLanes;
         const bool live = row < rows;
         const int64_t base = row * T::kChunks + sub;
