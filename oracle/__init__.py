@@ -24,7 +24,9 @@ Everything is plain numpy in float64, written from the definitions on the page
   partition (windows back to the grid, roll back, crop), which the pages imply
   but do not describe;
 * ``window_reverse_add_ln`` / ``add_norm_gather`` -- the residual add + norm of
-  section 4 fused with the reverse, or with the forward gather of section 5.
+  section 4 fused with the reverse, or with the forward gather of section 5;
+* ``bias_gelu`` -- the float32 bias + tanh-GELU of the page "PyTorch + HIP custom
+  fused operator" (Hygon DCU practice series), sections 3-6.
 
 Each function is pinned by ``tests/test_oracle_pins.py`` to closed forms,
 brute force on tiny inputs, a library routine, or values derived by hand and
@@ -32,6 +34,7 @@ stored under ``tests/golden/``.
 """
 from .rowops import (EPS, WIDTHS, fp16_round, residual_sum, layer_norm, add_ln, layer_norm_affine,
                      add_ln_affine)
+from .activation import bias_gelu
 from .window import (padded_extent, window_token_count, window_index_table,
                      window_gather, norm_gather, norm_gather_rows, window_reverse,
                      window_inverse_table, window_reverse_add_ln, add_norm_gather)
@@ -41,5 +44,5 @@ __all__ = [
     "add_ln_affine",
     "padded_extent", "window_token_count", "window_index_table", "window_gather",
     "norm_gather", "norm_gather_rows", "window_reverse", "window_inverse_table",
-    "window_reverse_add_ln", "add_norm_gather",
+    "window_reverse_add_ln", "add_norm_gather", "bias_gelu",
 ]

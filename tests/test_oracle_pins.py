@@ -466,3 +466,47 @@ def test_ln_affine_two_valued_closed_form():
     assert (bits_of(y[0, k:]) == bits_of(np.float16(float(yb)))).all()
     r, y2 = oracle.add_ln_affine(np.zeros_like(row), row, g, be)
     assert np.array_equal(bits_of(r), bits_of(row)) and np.array_equal(bits_of(y2), bits_of(y))
+
+
+# ---------------------------------------------------------------------------
+# bias + tanh-GELU (float32)
+
+
+def test_bias_gelu_matches_torch_float64():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(120)
+    x = rng.normal(0, 3, size=(257, 96)).astype(np.float32)
+    b = rng.normal(0, 1, size=96).astype(np.float32)
+    t = torch.from_numpy(x) + torch.from_numpy(b)                # the float32 add of the eager path
+    ref = torch.nn.functional.gelu(t.double(), approximate="tanh").numpy()
+    got = oracle.bias_gelu(x, b).astype(np.float64)
+    # both evaluate the same formula in float64; in the saturated negative tail
+    # 1 + tanh(z) cancels and the two differ by ~1e-16 absolute, nowhere else
+    assert np.allclose(got, ref.astype(np.float32).astype(np.float64), rtol=1e-7, atol=1e-15)
+    big = np.abs(ref) > 1e-6
+    assert np.array_equal(got[big], ref[big].astype(np.float32).astype(np.float64))
+    # a wrong constant or the exact (erf) GELU is far outside that agreement
+    erf = torch.nn.functional.gelu(t.double()).numpy()
+    assert np.abs(erf - ref).max() > 1e-4
+
+
+def test_bias_gelu_closed_forms():
+    x = np.array([[0.0, -0.0, 1.0, -1.0, 30.0, -30.0, np.inf, -np.inf, np.nan, 2.5]], np.float32)
+    y = oracle.bias_gelu(x, np.zeros(x.shape[1], np.float32))
+    assert y[0, 0] == 0.0 and y[0, 1] == 0.0
+    # g(t) - g(-t) = t exactly in real arithmetic (tanh is odd)
+    assert abs(float(y[0, 2]) - float(y[0, 3]) - 1.0) < 1e-6
+    assert y[0, 4] == np.float32(30.0) and y[0, 5] == 0.0        # saturation: t and -0
+    assert y[0, 6] == np.inf and np.isnan(y[0, 7]) and np.isnan(y[0, 8])
+    # tanh form at 1: 0.5 * (1 + tanh(sqrt(2/pi) * 1.044715)), worked out in high precision
+    getcontext().prec = 50
+    import math
+    z = math.sqrt(2 / math.pi) * 1.044715
+    assert abs(float(y[0, 2]) - 0.5 * (1 + math.tanh(z))) < 1e-7
+
+
+def test_bias_gelu_adds_the_bias_in_float32_first():
+    # 1 + 2**-30 rounds to 1 in float32: the activation must see exactly 1.0
+    x = np.array([[1.0]], np.float32)
+    b = np.array([2.0 ** -30], np.float32)
+    assert oracle.bias_gelu(x, b)[0, 0] == oracle.bias_gelu(x, np.zeros(1, np.float32))[0, 0]
