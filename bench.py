@@ -73,6 +73,8 @@ OPS = ("ln_fixed", "add_ln", "window_index_build", "window_gather", "norm_gather
 NEXT_OPS = ("window_inverse_build", "window_reverse_add_ln", "add_norm_gather", "ln_affine", "add_ln_affine")
 # the patch-merge LayerNorm (C = 768 on the level-2 grid), reported per kernel
 MERGE_OPS = ("ln_fixed", "ln_affine")
+# the float32 bias + tanh-GELU at the shapes of the HIP extension tutorial
+GELU_SHAPES = ((1024, 768), (4096, 1024), (8192, 2048))
 
 
 def level_inputs(level):
@@ -394,6 +396,31 @@ def main(argv=None):
         bytes_of[(PATCH_MERGE.name, op)] = algorithmic_bytes(op, PATCH_MERGE.tokens, PATCH_MERGE.tokens,
                                                              PATCH_MERGE.channels)
     kernels = {}
+    # the float32 bias + tanh-GELU at the HIP extension tutorial's shapes
+    for rows, cols in GELU_SHAPES:
+        nb = 2 * rows * cols * 4 + cols * 4
+        count = min(64, max(3, -(-COLD_BYTES // nb) + 1))
+        gen = torch.Generator(device="cpu").manual_seed(20260716)
+        xs = [torch.randn(rows, cols, generator=gen).to(dev) for _ in range(1)]
+        bias = torch.randn(cols, generator=gen).to(dev)
+        pool = []
+        for _ in range(count):
+            xi = xs[0].clone()
+            pool.append(lwg.prepare("bias_gelu", xi, bias, torch.empty_like(xi)))
+        f = lambda i, pool=pool: pool[i % len(pool)]()  # noqa: E731
+        for i in range(len(pool)):
+            f(i)
+        runs = np.array([run_timed(f, args.kernel_reps) for _ in range(5)])
+        del pool, f, xs
+        torch.cuda.empty_cache()
+        med = float(np.median(runs))
+        gbs = nb / (med * 1e-6) / 1e9
+        kernels[f"bias_gelu@{rows}x{cols}"] = {
+            "dtype": "f32", "rows_in": rows, "cols": cols, "in_step": False, "bytes": nb,
+            "avg_us": round(med, 2), "min_run_us": round(float(runs.min()), 2),
+            "max_run_us": round(float(runs.max()), 2), "GBps": round(gbs, 1),
+            "pct_of_peak": round(100 * gbs / PEAK_GBS, 1),
+        }
     for lv, ops in ((LEVEL1, OPS + NEXT_OPS), (LEVEL2, OPS + NEXT_OPS), (PATCH_MERGE, MERGE_OPS)):
         for op in ops:
             pool = pool_for(lv, op)

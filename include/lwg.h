@@ -199,6 +199,23 @@ int32_t lwg_add_ln_affine(const void* branch, const void* residual, const void* 
                           const void* beta, void* residual_out, void* y, int64_t rows,
                           int32_t C, double eps, void* stream);
 
+/*
+ * Bias + tanh-approximated GELU in float32 (the fused operator of the page
+ * "PyTorch + HIP custom fused operator", sections 3-6):
+ *   t = x[r, c] + bias[c]  (float32 add)
+ *   y[r, c] = 0.5 t (1 + tanh(sqrt(2/pi) (t + 0.044715 t^3)))
+ * evaluated as t / (1 + exp(-2z)) with the hardware exponential and
+ * reciprocal (within a few float32 ulp of the exact value; the page's gate is
+ * rtol = atol = 2e-5).
+ * x, y : device float32 [rows, cols], 16-byte aligned; y may equal x.
+ * bias : device float32 [cols], 16-byte aligned; must not overlap y.
+ * cols : a positive multiple of 4, and rows*cols/4 at most INT32_MAX.
+ * This operation is not part of the LayerNorm/gather path and takes float32,
+ * not binary16.
+ */
+int32_t lwg_bias_gelu(const void* x, const void* bias, void* y, int64_t rows, int32_t cols,
+                      void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* lwg_status_string(int32_t status);
 

@@ -27,6 +27,9 @@ and the window reverse that follows attention, plus the two fusions around it:
 and, for callers that keep the LayerNorm scale and shift:
   ln_affine(x, gamma, beta), add_ln_affine(branch, residual, gamma, beta)
 Widths: 192 and 384 (the model's), 768 (its patch-merge width).
+
+and the float32 bias + tanh-GELU of the HIP extension tutorial:
+  bias_gelu(x, bias)                 gelu_tanh(x + bias), float32
 """
 from __future__ import annotations
 
@@ -37,7 +40,7 @@ import torch
 from . import _lib
 from ._lib import LwgError
 
-__all__ = ["ln_fixed", "add_ln", "ln_affine", "add_ln_affine", "window_token_count", "window_index_build", "window_table",
+__all__ = ["ln_fixed", "add_ln", "ln_affine", "add_ln_affine", "bias_gelu", "window_token_count", "window_index_build", "window_table",
            "window_gather", "norm_gather", "window_inverse_build", "window_inverse_table",
            "window_reverse", "window_reverse_add_ln", "add_norm_gather", "LwgError", "WIDTHS", "EPS",
            "library"]
@@ -156,6 +159,31 @@ def add_ln_affine(branch: torch.Tensor, residual: torch.Tensor, gamma: torch.Ten
         _lib.check(lib.lwg_add_ln_affine(_ptr(branch), _ptr(residual), _ptr(gamma), _ptr(beta), _ptr(r), _ptr(y),
                                          rows, residual.shape[-1], float(eps), _stream(residual.device)))
     return r, y
+
+
+def bias_gelu(x: torch.Tensor, bias: torch.Tensor, out: torch.Tensor = None) -> torch.Tensor:
+    """float32 gelu(x + bias, tanh form) over the last dimension; ``out`` may be ``x``."""
+    for name, t in (("x", x), ("bias", bias)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float32:
+            raise RuntimeError(f"{name} must be a float32 tensor")
+        if not t.is_contiguous():
+            raise RuntimeError(f"{name} must be contiguous")
+        if t.device.type != "cuda":
+            raise RuntimeError(f"{name} must be on a GPU device, got {t.device}")
+    if x.dim() < 1 or bias.dim() != 1 or bias.numel() != x.shape[-1]:
+        raise RuntimeError("bias must be 1-D with one entry per column of x")
+    _same_device(x, ("bias", bias))
+    cols = x.shape[-1]
+    rows = x.numel() // cols if cols else 0
+    if out is None:
+        out = torch.empty_like(x)
+    elif out.dtype != torch.float32 or tuple(out.shape) != tuple(x.shape) or not out.is_contiguous() \
+            or out.device != x.device:
+        raise RuntimeError("out must be a contiguous float32 tensor shaped like x")
+    lib = _lib.load()
+    with torch.cuda.device(x.device):
+        _lib.check(lib.lwg_bias_gelu(_ptr(x), _ptr(bias), _ptr(out), rows, cols, _stream(x.device)))
+    return out
 
 
 def _triple(v, name):
@@ -445,6 +473,13 @@ def prepare(op: str, *tensors, eps: float = EPS, grid=None, window=None, shift=(
         dev = r.device
         fn, args = lib.lwg_add_ln_affine, (_ptr(br), _ptr(r), _ptr(g), _ptr(b), _ptr(ro), _ptr(y), rows,
                                            r.shape[-1], float(eps), _stream(dev))
+    elif op == "bias_gelu":
+        x, b, y = tensors
+        if x.dtype != torch.float32 or b.dtype != torch.float32 or y.dtype != torch.float32:
+            raise RuntimeError("bias_gelu takes float32 tensors")
+        dev = x.device
+        cols = x.shape[-1]
+        fn, args = lib.lwg_bias_gelu, (_ptr(x), _ptr(b), _ptr(y), x.numel() // cols, cols, _stream(dev))
     else:
         raise ValueError(f"unknown op {op!r}")
     return Prepared(fn, args, tensors)

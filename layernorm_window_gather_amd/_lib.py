@@ -38,6 +38,7 @@ SIGNATURES = {
     "lwg_window_reverse_add_ln": (_i32, [_p, _i64, _p, _p, _p, _p, _i64, _i32, _f64, _p]),
     "lwg_add_norm_gather": (_i32, [_p, _p, _p, _i64, _i32, _p, _i64, _f64, _p, _p]),
     "lwg_ln_affine": (_i32, [_p, _p, _p, _p, _i64, _i32, _f64, _p]),
+    "lwg_bias_gelu": (_i32, [_p, _p, _p, _i64, _i32, _p]),
     "lwg_add_ln_affine": (_i32, [_p, _p, _p, _p, _p, _p, _i64, _i32, _f64, _p]),
     "lwg_status_string": (ctypes.c_char_p, [_i32]),
     "lwg_last_error": (ctypes.c_char_p, []),

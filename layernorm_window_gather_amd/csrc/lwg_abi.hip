@@ -387,3 +387,23 @@ LWG_EXPORT int32_t lwg_add_ln_affine(const void* branch, const void* residual, c
                                                 static_cast<hipStream_t>(stream)),
                       fn);
 }
+
+LWG_EXPORT int32_t lwg_bias_gelu(const void* x, const void* bias, void* y, int64_t rows, int32_t cols,
+                                 void* stream) {
+    static const char* fn = "lwg_bias_gelu";
+    int32_t st;
+    if (cols < 4 || cols % 4 != 0)
+        return fail(LWG_ERR_INVALID_ARGUMENT, "%s: cols=%d must be a positive multiple of 4", fn, cols);
+    if (rows < 0 || rows > INT32_MAX || rows * static_cast<int64_t>(cols) / 4 > INT32_MAX)
+        return fail(LWG_ERR_INVALID_ARGUMENT, "%s: rows=%lld with cols=%d exceeds 2^31-1 float4 groups", fn,
+                    static_cast<long long>(rows), cols);
+    if (rows == 0) return ok();
+    if ((st = check_tensor(fn, "x", x)) || (st = check_tensor(fn, "bias", bias)) || (st = check_tensor(fn, "y", y)))
+        return st;
+    const uint64_t bytes = static_cast<uint64_t>(rows) * cols * 4;
+    if (!same_or_disjoint(x, y, bytes))
+        return fail(LWG_ERR_ALIASING, "%s: y partially overlaps x (only y == x is allowed)", fn);
+    if (overlap(y, bytes, bias, static_cast<uint64_t>(cols) * 4))
+        return fail(LWG_ERR_ALIASING, "%s: y overlaps bias", fn);
+    return hip_result(lwg::launch_bias_gelu(x, bias, y, rows, cols, static_cast<hipStream_t>(stream)), fn);
+}

@@ -581,6 +581,41 @@ __global__ __launch_bounds__(kBlock) void window_inverse_kernel(WindowGeometry g
 }
 
 // ---------------------------------------------------------------------------
+// Bias + tanh-GELU, float32 (the fused operator of the page "PyTorch + HIP
+// custom fused operator", sections 3-6): y = g(x + bias) with
+// g(t) = 0.5 t (1 + tanh z), z = sqrt(2/pi) (t + 0.044715 t^3).
+// Since 0.5 (1 + tanh z) = 1 / (1 + exp(-2z)), g(t) = t / (1 + exp(-2z)); the
+// exponential is the hardware base-2 one, exp(-2z) = 2^(-2 z log2 e), and the
+// division the hardware reciprocal. In the negative tail exp(-2z) grows to
+// +Inf and g goes to -0; for t = -Inf the product is NaN, as in the tanh form.
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float gelu_tanh(float t) {
+    constexpr float kMinus2ZLog2e = static_cast<float>(-2.0 * 0.79788456080286535588 * 1.44269504088896340736);
+    const float u = t * __builtin_fmaf(0.044715f, t * t, 1.0f);     // t + 0.044715 t^3
+    const float e = __builtin_amdgcn_exp2f(kMinus2ZLog2e * u);       // exp(-2z)
+    return t * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+template <class H>
+__global__ __launch_bounds__(kBlock) void bias_gelu_kernel(const f32x4_t* x, const f32x4_t* __restrict__ bias,
+                                                           f32x4_t* y, int64_t n4, FastDiv cols4) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < n4; i += stride) {
+        const uint32_t i32 = static_cast<uint32_t>(i);             // n4 < 2^31
+        const uint32_t col = i32 - fdiv(i32, cols4) * cols4.d;
+        f32x4_t v;
+        if constexpr (H::kNtLoad) v = __builtin_nontemporal_load(x + i);
+        else v = x[i];
+        const f32x4_t b = bias[col];
+        v = f32x4_t{gelu_tanh(v.x + b.x), gelu_tanh(v.y + b.y), gelu_tanh(v.z + b.z), gelu_tanh(v.w + b.w)};
+        if constexpr (H::kNtStore) __builtin_nontemporal_store(v, y + i);
+        else y[i] = v;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Launch configuration
 
 // Launch configuration, measured on MI355X with cache-cold buffers (every
@@ -776,6 +811,16 @@ hipError_t launch_add_ln_affine(const void* branch, const void* residual, const 
         return add_ln_affine_c<decltype(c)::value>(branch, residual, gamma, beta, residual_out, y, rows, eps,
                                                    stream);
     });
+}
+
+hipError_t launch_bias_gelu(const void* x, const void* bias, void* y, int64_t rows, int32_t cols,
+                            hipStream_t stream) {
+    const int64_t n4 = rows * cols / 4;
+    const unsigned grid = static_cast<unsigned>((n4 + kBlock - 1) / kBlock);
+    bias_gelu_kernel<Streaming><<<grid, kBlock, 0, stream>>>(
+        static_cast<const f32x4_t*>(x), static_cast<const f32x4_t*>(bias), static_cast<f32x4_t*>(y), n4,
+        make_fastdiv(static_cast<uint32_t>(cols / 4)));
+    return hipGetLastError();
 }
 
 }  // namespace lwg

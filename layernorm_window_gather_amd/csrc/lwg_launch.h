@@ -51,6 +51,8 @@ hipError_t launch_window_gather(const void* x, int64_t n_src, int32_t C, const i
 hipError_t launch_norm_gather(const void* x, int64_t n_src, int32_t C, const int32_t* table,
                               int64_t n_out, double eps, void* out, hipStream_t stream);
 hipError_t launch_window_inverse(const WindowGeometry& g, int32_t* inverse, hipStream_t stream);
+hipError_t launch_bias_gelu(const void* x, const void* bias, void* y, int64_t rows, int32_t cols,
+                            hipStream_t stream);
 hipError_t launch_ln_affine(const void* x, const void* gamma, const void* beta, void* y, int64_t rows,
                             int32_t C, double eps, hipStream_t stream);
 hipError_t launch_add_ln_affine(const void* branch, const void* residual, const void* gamma, const void* beta,

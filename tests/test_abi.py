@@ -246,3 +246,18 @@ def test_width_768_accepted_by_every_row_call(lib):
     # a 768-wide call that fails later validation proves the width itself passed
     assert lib.lwg_ln_fixed(None, B16, 10, 768, 1e-5, ST) == _lib.LWG_ERR_INVALID_ARGUMENT
     assert lib.lwg_window_gather(A16, 10, 768, None, 5, B16, ST) == _lib.LWG_ERR_INVALID_ARGUMENT
+
+
+def test_bias_gelu_validation(lib):
+    S = _lib
+    f = lib.lwg_bias_gelu
+    X, Bi, Y = P(0x100000), P(0x200000), P(0x300000)
+    assert f(X, Bi, Y, 10, 6, ST) == S.LWG_ERR_INVALID_ARGUMENT        # cols not a multiple of 4
+    assert f(X, Bi, Y, 10, 0, ST) == S.LWG_ERR_INVALID_ARGUMENT
+    assert f(X, Bi, Y, -1, 8, ST) == S.LWG_ERR_INVALID_ARGUMENT
+    assert f(X, Bi, Y, 2**30, 16, ST) == S.LWG_ERR_INVALID_ARGUMENT    # more than 2^31-1 float4 groups
+    assert f(X, None, Y, 10, 8, ST) == S.LWG_ERR_INVALID_ARGUMENT
+    assert f(X, P(0x200004), Y, 10, 8, ST) == S.LWG_ERR_MISALIGNED
+    assert f(X, Bi, P(0x100000 + 32), 10, 8, ST) == S.LWG_ERR_ALIASING  # partial overlap with x
+    assert f(X, Bi, P(0x200000 - 16), 10, 8, ST) == S.LWG_ERR_ALIASING  # y over the bias
+    assert f(None, None, None, 0, 8, ST) == S.LWG_OK
