@@ -269,7 +269,7 @@ def main(argv=None):
     ap.add_argument("--kernel-reps", type=int, default=40, help="back-to-back launches per timed run")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="minimum oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=OPS + ("all",), default=None,
+    ap.add_argument("--only", choices=OPS + NEXT_OPS + ("all",), default=None,
                     help="launch only this op (or every op), --steps times per level (profiling runs)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="also run an elementwise copy of this many MiB (PMC calibration)")
@@ -314,11 +314,22 @@ def main(argv=None):
     stream = torch.cuda.current_stream(dev)
 
     if args.only:
-        only = OPS if args.only == "all" else (args.only,)
+        only = OPS + NEXT_OPS if args.only == "all" else (args.only,)
         for lv in levels:
+            xd, rd = (torch.from_numpy(a).to(dev) for a in host[lv.name])
+            table = sets[0][lv.name].table
             for op in only:
+                calls = [sets[i][lv.name].calls[op] for i in range(args.sets)] if op in OPS else \
+                    op_pool(lwg, torch, dev, lv, op, xd, rd, table, m_of[lv.name], 1 << 40)
                 for i in range(args.warmup + args.steps):
-                    sets[i % args.sets][lv.name].calls[op]()
+                    calls[i % len(calls)]()
+        if args.only == "all":
+            gen = torch.Generator(device="cpu").manual_seed(1)
+            for rows, cols in GELU_SHAPES[-1:]:
+                xg, bg = torch.randn(rows, cols, generator=gen).to(dev), torch.randn(cols, generator=gen).to(dev)
+                call = lwg.prepare("bias_gelu", xg, bg, torch.empty_like(xg))
+                for _ in range(args.warmup + args.steps):
+                    call()
         torch.cuda.synchronize()
         if args.calibration_copy_mib:
             n = args.calibration_copy_mib * (1 << 20) // 2
