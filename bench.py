@@ -238,17 +238,26 @@ def cpu_baseline(step_bytes, host, levels, min_seconds):
     same workload, repeated until at least ``min_seconds`` have passed (at most
     30 steps); reported in GB/s of algorithmic bytes."""
     import oracle
+    per_op = {}
+
+    def timed(key, fn, *a):
+        t = time.perf_counter()
+        out = fn(*a)
+        if repeats == 1:
+            per_op[key] = round(time.perf_counter() - t, 4)
+        return out
+
     t0 = time.perf_counter()
     repeats = 0
     while repeats < 30 and (repeats == 0 or time.perf_counter() - t0 < min_seconds):
         repeats += 1
         for lv in levels:
             x, residual = host[lv.name]
-            oracle.layer_norm(x)
-            oracle.add_ln(x, residual)
-            table = oracle.window_index_table(lv.grid, WINDOW, SHIFT)
-            oracle.window_gather(x, table)
-            oracle.norm_gather(x, table)
+            timed(f"ln_fixed@{lv.name}", oracle.layer_norm, x)
+            timed(f"add_ln@{lv.name}", oracle.add_ln, x, residual)
+            table = timed(f"window_index_build@{lv.name}", oracle.window_index_table, lv.grid, WINDOW, SHIFT)
+            timed(f"window_gather@{lv.name}", oracle.window_gather, x, table)
+            timed(f"norm_gather@{lv.name}", oracle.norm_gather, x, table)
     dt = time.perf_counter() - t0
     return {
         "value": round(step_bytes * repeats / dt / 1e9, 4),
@@ -256,7 +265,9 @@ def cpu_baseline(step_bytes, host, levels, min_seconds):
         "cores": 1,
         "kind": "oracle",
         "sample": f"{repeats} full step(s) of the same workload (both levels, all five ops) "
-                  f"in {dt:.1f} s; numpy ufuncs run on one thread; host has {os.cpu_count()} logical CPUs",
+                  f"in {dt:.1f} s; numpy ufuncs run on one thread; host has {os.cpu_count()} logical CPUs, "
+                  f"{len(os.sched_getaffinity(0))} in this process's affinity set",
+        "per_op_seconds_first_step": per_op,
     }
 
 

@@ -1,12 +1,16 @@
 // Row kernels for gfx950 (CDNA4, wave64): fixed-width LayerNorm, residual add +
-// LayerNorm, shifted-window index tables, window gather and fused norm-gather.
+// LayerNorm, shifted-window index tables, window gather, fused norm-gather, and
+// the steps around them (window reverse fused with add + LayerNorm, add +
+// LayerNorm + gather, affine LayerNorm, float32 bias + tanh-GELU).
 //
 // What is computed follows the page "Pangu-Weather inference optimisation on
 // Hygon BW1000 (gfx936)" (l189.com/news/2144533):
-//   section 3 -- LayerNorm over rows of width 192 or 384, FP16 in and out, no affine;
+//   section 3 -- LayerNorm over rows of width 192 or 384 (and the model's
+//                patch-merge width 768), FP16 in and out, no affine;
 //   section 4 -- residual add whose FP16 rounding is kept, then LayerNorm of it;
 //   section 5 -- INT32 window index tables (-1 = padding row = zeros), a gather
-//                driven by them, and the norm-gather fusion.
+//                driven by them, and the norm-gather fusion;
+// and the bias + GELU of the page "PyTorch + HIP custom fused operator".
 // How it is computed is designed for CDNA4 rather than taken from that page
 // (which used one wave per row and __half2 moves on gfx936):
 //   * Every access is a 16-byte (8 x binary16) vector load or store. A row of C
@@ -22,7 +26,8 @@
 //     practice, where FP32 arithmetic flips about 1e-4 of outputs by one ulp.
 //     The final binary64 -> binary16 rounding goes through a round-to-odd
 //     binary32 intermediate, which makes the two-step conversion exact-once.
-//   * All kernels are stateless and row-local: no atomics, no shared memory.
+//   * All kernels are stateless and row-local: no atomics, no scratch memory.
+//     Only the affine kernels use LDS, to hold gamma and beta for a workgroup.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -214,9 +219,9 @@ __device__ __forceinline__ void layer_norm_lane(chunk_t (&v)[K], double eps) {
 }
 
 // Affine LayerNorm: ((x - mean) / sqrt(var + eps)) * gamma + beta in binary64,
-// rounded once to binary16. gamma and beta are binary16 [C]; this lane reads its
-// columns chunk by chunk as it writes them (small arrays that stay in cache), so
-// only one chunk of them is live next to the row's deviations.
+// rounded once to binary16. gamma and beta are binary16 [C] (held in LDS by the
+// affine kernels); this lane reads its columns chunk by chunk as it writes them,
+// so only one chunk of them is live next to the row's deviations.
 template <int C, int K>
 __device__ __forceinline__ void layer_norm_affine_lane(chunk_t (&v)[K], const chunk_t* gamma,
                                                        const chunk_t* beta, int sub, double eps) {
@@ -251,7 +256,6 @@ __device__ __forceinline__ void zero(chunk_t (&v)[K]) {
 // The launcher sizes the grid either to one tile per wave or to a fixed number
 // of resident workgroups.
 
-template <class T>
 __device__ __forceinline__ int64_t first_wave() {
     return static_cast<int64_t>(blockIdx.x) * (kBlock / 64) + (threadIdx.x >> 6);
 }
@@ -268,7 +272,7 @@ __global__ __launch_bounds__(kBlock) void ln_fixed_kernel(const chunk_t* x, chun
     using T = Tile<C, K>;
     const int lane = threadIdx.x & 63;
     const int sub = lane % T::kLanes;
-    for (int64_t w = first_wave<T>(); w * T::kRowsPerWave < rows; w += wave_stride()) {
+    for (int64_t w = first_wave(); w * T::kRowsPerWave < rows; w += wave_stride()) {
         const int64_t row = w * T::kRowsPerWave + lane / T::kLanes;
         const bool live = row < rows;
         const int64_t base = row * T::kChunks + sub;
@@ -293,7 +297,7 @@ __global__ __launch_bounds__(kBlock) void add_ln_kernel(const chunk_t* branch, c
     using T = Tile<C, K>;
     const int lane = threadIdx.x & 63;
     const int sub = lane % T::kLanes;
-    for (int64_t w = first_wave<T>(); w * T::kRowsPerWave < rows; w += wave_stride()) {
+    for (int64_t w = first_wave(); w * T::kRowsPerWave < rows; w += wave_stride()) {
         const int64_t row = w * T::kRowsPerWave + lane / T::kLanes;
         const bool live = row < rows;
         const int64_t base = row * T::kChunks + sub;
@@ -345,7 +349,7 @@ __global__ __launch_bounds__(kBlock) void ln_affine_kernel(const chunk_t* x, con
     beta = params + T::kChunks;
     const int lane = threadIdx.x & 63;
     const int sub = lane % T::kLanes;
-    for (int64_t w = first_wave<T>(); w * T::kRowsPerWave < rows; w += wave_stride()) {
+    for (int64_t w = first_wave(); w * T::kRowsPerWave < rows; w += wave_stride()) {
         // re-read gamma/beta from LDS per row tile instead of letting the
         // compiler hoist 2*K widened chunks out of the loop into registers
         asm volatile("" ::: "memory");
@@ -378,7 +382,7 @@ __global__ __launch_bounds__(kBlock) void add_ln_affine_kernel(const chunk_t* br
     beta = params + T::kChunks;
     const int lane = threadIdx.x & 63;
     const int sub = lane % T::kLanes;
-    for (int64_t w = first_wave<T>(); w * T::kRowsPerWave < rows; w += wave_stride()) {
+    for (int64_t w = first_wave(); w * T::kRowsPerWave < rows; w += wave_stride()) {
         asm volatile("" ::: "memory");  // as in ln_affine_kernel: no hoisting of gamma/beta
         const int64_t row = w * T::kRowsPerWave + lane / T::kLanes;
         const bool live = row < rows;
@@ -417,7 +421,7 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(const chunk_t* __restric
     using T = Tile<C, K>;
     const int lane = threadIdx.x & 63;
     const int sub = lane % T::kLanes;
-    for (int64_t w = first_wave<T>(); w * T::kRowsPerWave < n_out; w += wave_stride()) {
+    for (int64_t w = first_wave(); w * T::kRowsPerWave < n_out; w += wave_stride()) {
         const int64_t j = w * T::kRowsPerWave + lane / T::kLanes;
         const bool live = j < n_out;
         const int32_t t = live ? table[j] : -1;
@@ -450,7 +454,7 @@ __global__ __launch_bounds__(kBlock) void reverse_add_ln_kernel(
     using T = Tile<C, K>;
     const int lane = threadIdx.x & 63;
     const int sub = lane % T::kLanes;
-    for (int64_t w = first_wave<T>(); w * T::kRowsPerWave < rows; w += wave_stride()) {
+    for (int64_t w = first_wave(); w * T::kRowsPerWave < rows; w += wave_stride()) {
         const int64_t row = w * T::kRowsPerWave + lane / T::kLanes;
         const bool live = row < rows;
         const int32_t t = live ? idx[row] : -1;
@@ -494,7 +498,7 @@ __global__ __launch_bounds__(kBlock) void add_norm_gather_kernel(
     using T = Tile<C, K>;
     const int lane = threadIdx.x & 63;
     const int sub = lane % T::kLanes;
-    for (int64_t w = first_wave<T>(); w * T::kRowsPerWave < n_out; w += wave_stride()) {
+    for (int64_t w = first_wave(); w * T::kRowsPerWave < n_out; w += wave_stride()) {
         const int64_t j = w * T::kRowsPerWave + lane / T::kLanes;
         const bool live = j < n_out;
         const int32_t t = live ? table[j] : -1;
