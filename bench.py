@@ -216,6 +216,27 @@ def parity_gate(lwg, torch, sets, host, levels, m_of):
     return True
 
 
+def memory_attributes(dev_index: int):
+    """The device's reported memory clock (kHz) and bus width (bits), read with
+    hipDeviceGetAttribute, and the figure clock x bus width x 2 transfers per
+    clock. HBM3E moves more than two transfers per reported clock, so that
+    figure sits below the published peak; the fractions use the published
+    8 TB/s."""
+    import ctypes
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+    except OSError:
+        return None
+    bus, clk = ctypes.c_int(0), ctypes.c_int(0)
+    # hipDeviceAttributeMemoryBusWidth = 59, hipDeviceAttributeMemoryClockRate = 60
+    if hip.hipDeviceGetAttribute(ctypes.byref(bus), 59, dev_index) != 0 or \
+            hip.hipDeviceGetAttribute(ctypes.byref(clk), 60, dev_index) != 0:
+        return None
+    return {"memory_clock_khz": clk.value, "memory_bus_bits": bus.value,
+            "clock_x_bus_x2_GBps": round(clk.value * 1e3 * 2 * bus.value / 8 / 1e9, 1),
+            "published_peak_GBps": PEAK_GBS}
+
+
 def kernel_source_hash() -> str:
     return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
 
@@ -243,8 +264,7 @@ def cpu_baseline(step_bytes, host, levels, min_seconds):
     def timed(key, fn, *a):
         t = time.perf_counter()
         out = fn(*a)
-        if repeats == 1:
-            per_op[key] = round(time.perf_counter() - t, 4)
+        per_op.setdefault(key, []).append(time.perf_counter() - t)
         return out
 
     t0 = time.perf_counter()
@@ -253,12 +273,21 @@ def cpu_baseline(step_bytes, host, levels, min_seconds):
         repeats += 1
         for lv in levels:
             x, residual = host[lv.name]
-            timed(f"ln_fixed@{lv.name}", oracle.layer_norm, x)
-            timed(f"add_ln@{lv.name}", oracle.add_ln, x, residual)
-            table = timed(f"window_index_build@{lv.name}", oracle.window_index_table, lv.grid, WINDOW, SHIFT)
-            timed(f"window_gather@{lv.name}", oracle.window_gather, x, table)
-            timed(f"norm_gather@{lv.name}", oracle.norm_gather, x, table)
+            timed(("ln_fixed", lv), oracle.layer_norm, x)
+            timed(("add_ln", lv), oracle.add_ln, x, residual)
+            table = timed(("window_index_build", lv), oracle.window_index_table, lv.grid, WINDOW, SHIFT)
+            timed(("window_gather", lv), oracle.window_gather, x, table)
+            timed(("norm_gather", lv), oracle.norm_gather, x, table)
     dt = time.perf_counter() - t0
+    ops = {}
+    for (op, lv), times in per_op.items():
+        med = float(np.median(times))
+        m = oracle.window_token_count(lv.grid, WINDOW)
+        ops[f"{op}@{lv.name}"] = {
+            "median_s": round(med, 4), "runs": len(times),
+            "GBps": round(algorithmic_bytes(op, lv.tokens, m, lv.channels) / med / 1e9, 4),
+            "Mtokens_per_s": round(lv.tokens / med / 1e6, 3),
+        }
     return {
         "value": round(step_bytes * repeats / dt / 1e9, 4),
         "unit": "GB/s",
@@ -267,7 +296,7 @@ def cpu_baseline(step_bytes, host, levels, min_seconds):
         "sample": f"{repeats} full step(s) of the same workload (both levels, all five ops) "
                   f"in {dt:.1f} s; numpy ufuncs run on one thread; host has {os.cpu_count()} logical CPUs, "
                   f"{len(os.sched_getaffinity(0))} in this process's affinity set",
-        "per_op_seconds_first_step": per_op,
+        "per_op": ops,
     }
 
 
@@ -359,6 +388,18 @@ def main(argv=None):
             for op in OPS:
                 calls[op]()
 
+    def wall_single(launch, count=20):
+        """Median host wall time of one launch bracketed by two synchronisations
+        (the way the pages time an operator); includes launch latency."""
+        times = []
+        for i in range(count):
+            torch.cuda.synchronize()
+            t = time.perf_counter()
+            launch(i)
+            torch.cuda.synchronize()
+            times.append(time.perf_counter() - t)
+        return float(np.median(times)) * 1e6
+
     def run_timed(launch, count, spin=True):
         """HIP events on the launch stream around `count` back-to-back launches;
         returns the average microseconds per launch. A spin kernel queued first
@@ -433,6 +474,7 @@ def main(argv=None):
         for i in range(len(pool)):
             f(i)
         runs = np.array([run_timed(f, args.kernel_reps) for _ in range(5)])
+        wall_us = wall_single(f)
         del pool, f, xs
         torch.cuda.empty_cache()
         med = float(np.median(runs))
@@ -441,7 +483,7 @@ def main(argv=None):
             "dtype": "f32", "rows_in": rows, "cols": cols, "in_step": False, "bytes": nb,
             "avg_us": round(med, 2), "min_run_us": round(float(runs.min()), 2),
             "max_run_us": round(float(runs.max()), 2), "GBps": round(gbs, 1),
-            "pct_of_peak": round(100 * gbs / PEAK_GBS, 1),
+            "pct_of_peak": round(100 * gbs / PEAK_GBS, 1), "wall_us_sync": round(wall_us, 2),
         }
     for lv, ops in ((LEVEL1, OPS + NEXT_OPS), (LEVEL2, OPS + NEXT_OPS), (PATCH_MERGE, MERGE_OPS)):
         for op in ops:
@@ -450,6 +492,7 @@ def main(argv=None):
             for i in range(len(pool)):
                 f(i)
             runs = np.array([run_timed(f, args.kernel_reps) for _ in range(5)])
+            wall_us = wall_single(f)
             del pool, f
             torch.cuda.empty_cache()
             med = float(np.median(runs))
@@ -462,6 +505,7 @@ def main(argv=None):
                 "min_run_us": round(float(runs.min()), 2), "max_run_us": round(float(runs.max()), 2),
                 "GBps": round(gbs, 1), "pct_of_peak": round(100 * gbs / PEAK_GBS, 1),
                 "Mtokens_per_s": round(lv.tokens / (med * 1e-6) / 1e6, 1),
+                "wall_us_sync": round(wall_us, 2),
             }
 
     # block-stack replay: 66 dependent calls on resident residual streams
@@ -514,6 +558,10 @@ def main(argv=None):
             "step_device_us": round(step_dev_us, 2),
             "buffer_sets": args.sets, "device": props.name,
             "arch": getattr(props, "gcnArchName", "?"), "cus": props.multi_processor_count,
+            "memory": memory_attributes(dev.index or 0),
+            "seeds": {"level1": 1, "level2": 2, "patch_merge_rows": 11, "patch_merge_values": 12,
+                      "replay_streams": 4, "replay_branch_of_block_b": "4 + b",
+                      "bias_gelu_torch_cpu_generator": 20260716},
         },
         "roofline": {
             "kernel": "add_ln@level1",

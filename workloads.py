@@ -164,3 +164,29 @@ def replay_branch(call: ReplayCall, near_constant: np.ndarray, offset: np.ndarra
     with offset rows drawn around 0 so the stream's offset rows keep their mean."""
     lv = call.level
     return mixed_rows(call.seed, lv.tokens, lv.channels, near_constant, offset, offset_mean=0.0)
+
+
+# Grids whose tensors pass 2**31 elements and 2**32 bytes (64-bit offsets),
+# with ragged extents so the window tables pad at both levels' widths.
+LARGE_192 = Level("large_192", (8, 1093, 1297), 192)   # 11,340,968 rows, 4.35 GB
+LARGE_384 = Level("large_384", (4, 1093, 1297), 384)   # 5,670,484 rows, 4.35 GB
+
+
+def id_tagged_rows(seed: int, rows: int, channels: int, block: int = 4096) -> np.ndarray:
+    """``[rows, channels]`` float16 whose rows are all distinct and carry their own
+    index: columns 0..2 hold the base-1024 digits of the row index (exact binary16
+    integers, least significant first), column 3 holds 1.0 as a marker, and
+    columns 4.. repeat a block of ``block`` i.i.d. N(0,1) rows. Built in place,
+    block by block, so a multi-GB array costs one pass over memory."""
+    rng = np.random.default_rng(seed)
+    base = _f16(rng.normal(0.0, 1.0, size=(block, channels)))
+    out = np.empty((rows, channels), np.float16)
+    for s in range(0, rows, block):
+        e = min(rows, s + block)
+        out[s:e] = base[: e - s]
+    ids = np.arange(rows, dtype=np.int64)
+    out[:, 0] = ids % 1024
+    out[:, 1] = (ids >> 10) % 1024
+    out[:, 2] = ids >> 20
+    out[:, 3] = 1.0
+    return out
