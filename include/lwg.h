@@ -10,8 +10,9 @@
  * "PyTorch + HIP custom fused operator" (Hygon DCU practice series), section 6.
  *
  * Conventions shared by every call:
- *  - Tensors are contiguous row-major [rows, C] arrays of IEEE 754 binary16.
- *    Token rows of a (Z,H,W) grid are stored in (z,h,w) order, z slowest.
+ *  - Tensors are contiguous row-major [rows, C] arrays of IEEE 754 binary16
+ *    (lwg_bias_gelu alone takes float32). Token rows of a (Z,H,W) grid are
+ *    stored in (z,h,w) order, z slowest.
  *  - Every tensor pointer is a device pointer, 16-byte aligned, allocated and
  *    freed by the caller. The library never allocates, frees, synchronises or
  *    changes the current device.
@@ -28,8 +29,14 @@
  *    width returns LWG_ERR_UNSUPPORTED_WIDTH.
  *  - Statistics (row mean and biased variance) are accumulated in binary64 from
  *    the binary16 inputs and each output is rounded once to binary16, to
- *    nearest-even. LayerNorm has no scale or shift: the BW1000 page folds the
- *    affine parameters into the following Linear at load time.
+ *    nearest-even. The plain LayerNorm calls have no scale or shift (the
+ *    BW1000 page folds the affine parameters into the following Linear at load
+ *    time); lwg_ln_affine and lwg_add_ln_affine apply them for callers that
+ *    do not fold.
+ *  - Calls only enqueue kernels on `stream`, so they may be recorded by HIP
+ *    stream capture into a graph and replayed. Calls on different threads
+ *    are independent; lwg_last_error() is per thread. Calls that overlap on
+ *    the device must not write the same memory.
  *  - Faults inside a kernel surface at the caller's next synchronisation.
  */
 #ifndef LWG_H

@@ -31,6 +31,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "lwg_launch.h"
@@ -651,7 +652,24 @@ template <int C, Op O> struct Launch { using H = Streaming; static constexpr int
 template <> struct Launch<384, Op::kNormGather> { using H = Streaming; static constexpr int kBlocksPerCu = 4; };
 
 
-int g_cus = 0;  // compute units of the current device, read once
+// Compute units of the device, queried on first use (0 = not yet known). Only
+// the launch shape of capped grids depends on it, never a result; a failed
+// query falls back to the MI355X count and clears HIP's last-error state so the
+// launch check that follows does not report it.
+std::atomic<int> g_cus{0};
+
+inline int compute_units() {
+    int cus = g_cus.load(std::memory_order_relaxed);
+    if (cus > 0) return cus;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+        (void)hipGetLastError();
+        cus = 256;
+    }
+    g_cus.store(cus, std::memory_order_relaxed);
+    return cus;
+}
 
 template <int C, Op O>
 unsigned grid_for(int64_t rows) {
@@ -659,16 +677,7 @@ unsigned grid_for(int64_t rows) {
     const int64_t tiles = (rows + T::kRowsPerWave - 1) / T::kRowsPerWave;
     int64_t blocks = (tiles + (kBlock / 64) - 1) / (kBlock / 64);
     if (Launch<C, O>::kBlocksPerCu > 0) {
-        if (g_cus == 0) {
-            int dev = 0, cus = 0;
-            if (hipGetDevice(&dev) == hipSuccess &&
-                hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-                cus > 0)
-                g_cus = cus;
-            else
-                g_cus = 256;
-        }
-        const int64_t cap = static_cast<int64_t>(g_cus) * Launch<C, O>::kBlocksPerCu;
+        const int64_t cap = static_cast<int64_t>(compute_units()) * Launch<C, O>::kBlocksPerCu;
         if (blocks > cap) blocks = cap;
     }
     return static_cast<unsigned>(blocks);

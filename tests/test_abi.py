@@ -261,3 +261,17 @@ def test_bias_gelu_validation(lib):
     assert f(X, Bi, P(0x100000 + 32), 10, 8, ST) == S.LWG_ERR_ALIASING  # partial overlap with x
     assert f(X, Bi, P(0x200000 - 16), 10, 8, ST) == S.LWG_ERR_ALIASING  # y over the bias
     assert f(None, None, None, 0, 8, ST) == S.LWG_OK
+
+
+def test_header_is_strict_c99(tmp_path):
+    """include/lwg.h compiles as C99 with -pedantic -Werror (no C++ in the ABI)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    src = tmp_path / "use_header.c"
+    src.write_text('#include "lwg.h"\nint main(void) { return lwg_abi_version() == LWG_ABI_VERSION ? 0 : 1; }\n')
+    res = subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-fsyntax-only",
+                          "-I", os.path.join(ROOT, "include"), str(src)], capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
