@@ -38,6 +38,7 @@ HALF = 2                   # bytes per binary16
 INDEX = 4                  # bytes per int32 table entry
 PMC_FILE = os.path.join(ROOT, "profiles", "add_ln_level1_pmc.json")
 KERNEL_SOURCE = os.path.join(ROOT, "layernorm_window_gather_amd", "csrc", "lwg_kernels.hip")
+BUILD_SCRIPT = os.path.join(ROOT, "layernorm_window_gather_amd", "build.py")
 
 
 def algorithmic_bytes(op: str, n: int, m: int, c: int) -> int:
@@ -238,7 +239,12 @@ def memory_attributes(dev_index: int):
 
 
 def kernel_source_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+    """Hash of what the kernel binary is built from: the kernel source and the
+    build script (compiler flags)."""
+    h = hashlib.sha256()
+    for path in (KERNEL_SOURCE, BUILD_SCRIPT):
+        h.update(open(path, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def traffic_from_profile(dominant_bytes):

@@ -31,6 +31,11 @@ def command(out: str = LIB) -> list:
         "-fvisibility=hidden", "-ffp-contract=on", "-Wall", "-Wno-unused-function",
         # no packed FP32 instructions anywhere in the device code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # kernel arguments preloaded into SGPRs at wave launch (gfx950 supports it;
+        # the code object keeps a loading prologue for firmware that does not):
+        # removes the first kernarg load from every wave's start, 1-4% on most
+        # row kernels
+        "-mllvm", "-amdgpu-kernarg-preload-count=16",
         "-I", os.path.join(ROOT, "include"), "-I", CSRC,
         *[os.path.join(CSRC, s) for s in SOURCES],
         "-o", out,
