@@ -265,62 +265,110 @@ __device__ __forceinline__ int64_t wave_stride() {
     return static_cast<int64_t>(gridDim.x) * (kBlock / 64);
 }
 
-// y may alias x: a lane reads all of its chunks before the row statistics
-// exist, and writes only the chunks it read.
+// The K chunks this lane holds of row tile w (zeros past the last row).
 template <int C, int K, class H>
-__global__ __launch_bounds__(kBlock) void ln_fixed_kernel(const chunk_t* x, chunk_t* y,
-                                                          int64_t rows, double eps) {
+__device__ __forceinline__ void load_tile(const chunk_t* x, int64_t w, int64_t rows, int lane,
+                                          chunk_t (&v)[K]) {
     using T = Tile<C, K>;
-    const int lane = threadIdx.x & 63;
-    const int sub = lane % T::kLanes;
-    for (int64_t w = first_wave(); w * T::kRowsPerWave < rows; w += wave_stride()) {
-        const int64_t row = w * T::kRowsPerWave + lane / T::kLanes;
-        const bool live = row < rows;
-        const int64_t base = row * T::kChunks + sub;
-        chunk_t v[K];
-        zero(v);
-        if (live) {
+    const int64_t row = w * T::kRowsPerWave + lane / T::kLanes;
+    zero(v);
+    if (row < rows) {
+        const int64_t base = row * T::kChunks + lane % T::kLanes;
 #pragma unroll
-            for (int k = 0; k < K; ++k) v[k] = load16<H>(x + base + k * T::kLanes);
-        }
-        layer_norm_lane<C, K>(v, eps);
-        if (live) {
-#pragma unroll
-            for (int k = 0; k < K; ++k) store16<H>(y + base + k * T::kLanes, v[k]);
-        }
+        for (int k = 0; k < K; ++k) v[k] = load16<H>(x + base + k * T::kLanes);
     }
 }
 
 template <int C, int K, class H>
+__device__ __forceinline__ void store_tile(chunk_t* y, int64_t w, int64_t rows, int lane,
+                                           const chunk_t (&v)[K]) {
+    using T = Tile<C, K>;
+    const int64_t row = w * T::kRowsPerWave + lane / T::kLanes;
+    if (row < rows) {
+        const int64_t base = row * T::kChunks + lane % T::kLanes;
+#pragma unroll
+        for (int k = 0; k < K; ++k) store16<H>(y + base + k * T::kLanes, v[k]);
+    }
+}
+
+// y may alias x: a lane reads all of its chunks before the row statistics
+// exist, and writes only the chunks it read. With kPrefetch a wave issues the
+// loads of its next tile before it normalises the current one, so on a grid
+// smaller than the tile count the arithmetic of one tile overlaps the memory
+// traffic of the next. (In place, the next tile's rows are other rows, read
+// before this tile's stores: still no overlap between a lane's reads and
+// another lane's writes.)
+template <int C, int K, class H, bool kPrefetch>
+__global__ __launch_bounds__(kBlock) void ln_fixed_kernel(const chunk_t* x, chunk_t* y,
+                                                          int64_t rows, double eps) {
+    using T = Tile<C, K>;
+    const int lane = threadIdx.x & 63;
+    if constexpr (kPrefetch) {
+        const int64_t stride = wave_stride();
+        int64_t w = first_wave();
+        chunk_t v[K];
+        load_tile<C, K, H>(x, w, rows, lane, v);
+        for (; w * T::kRowsPerWave < rows; w += stride) {
+            chunk_t next[K];
+            load_tile<C, K, H>(x, w + stride, rows, lane, next);
+            layer_norm_lane<C, K>(v, eps);
+            store_tile<C, K, H>(y, w, rows, lane, v);
+#pragma unroll
+            for (int k = 0; k < K; ++k) v[k] = next[k];
+        }
+    } else {
+        const int sub = lane % T::kLanes;
+        for (int64_t w = first_wave(); w * T::kRowsPerWave < rows; w += wave_stride()) {
+            const int64_t row = w * T::kRowsPerWave + lane / T::kLanes;
+            const bool live = row < rows;
+            const int64_t base = row * T::kChunks + sub;
+            chunk_t v[K];
+            zero(v);
+            if (live) {
+#pragma unroll
+                for (int k = 0; k < K; ++k) v[k] = load16<H>(x + base + k * T::kLanes);
+            }
+            layer_norm_lane<C, K>(v, eps);
+            if (live) {
+#pragma unroll
+                for (int k = 0; k < K; ++k) store16<H>(y + base + k * T::kLanes, v[k]);
+            }
+        }
+    }
+}
+
+// residual_out and y may alias the inputs: each lane reads its chunks of a row
+// before it writes any, and the prefetched tile is a different set of rows.
+template <int C, int K, class H, bool kPrefetch>
 __global__ __launch_bounds__(kBlock) void add_ln_kernel(const chunk_t* branch, const chunk_t* residual,
                                                         chunk_t* residual_out, chunk_t* y,
                                                         int64_t rows, double eps) {
     using T = Tile<C, K>;
     const int lane = threadIdx.x & 63;
-    const int sub = lane % T::kLanes;
-    for (int64_t w = first_wave(); w * T::kRowsPerWave < rows; w += wave_stride()) {
-        const int64_t row = w * T::kRowsPerWave + lane / T::kLanes;
-        const bool live = row < rows;
-        const int64_t base = row * T::kChunks + sub;
-        chunk_t b[K], r[K];
-        zero(b);
-        zero(r);
-        if (live) {
-#pragma unroll
-            for (int k = 0; k < K; ++k) {
-                b[k] = load16<H>(branch + base + k * T::kLanes);
-                r[k] = load16<H>(residual + base + k * T::kLanes);
-            }
+    const int64_t stride = wave_stride();
+    int64_t w = first_wave();
+    chunk_t b[K], r[K];
+    load_tile<C, K, H>(branch, w, rows, lane, b);
+    load_tile<C, K, H>(residual, w, rows, lane, r);
+    for (; w * T::kRowsPerWave < rows; w += stride) {
+        chunk_t nb[K], nr[K];
+        if constexpr (kPrefetch) {
+            load_tile<C, K, H>(branch, w + stride, rows, lane, nb);
+            load_tile<C, K, H>(residual, w + stride, rows, lane, nr);
         }
         residual_add<K>(b, r);
-        if (live) {
-#pragma unroll
-            for (int k = 0; k < K; ++k) store16<H>(residual_out + base + k * T::kLanes, r[k]);
-        }
+        store_tile<C, K, H>(residual_out, w, rows, lane, r);
         layer_norm_lane<C, K>(r, eps);
-        if (live) {
+        store_tile<C, K, H>(y, w, rows, lane, r);
+        if constexpr (kPrefetch) {
 #pragma unroll
-            for (int k = 0; k < K; ++k) store16<H>(y + base + k * T::kLanes, r[k]);
+            for (int k = 0; k < K; ++k) {
+                b[k] = nb[k];
+                r[k] = nr[k];
+            }
+        } else {
+            load_tile<C, K, H>(branch, w + stride, rows, lane, b);
+            load_tile<C, K, H>(residual, w + stride, rows, lane, r);
         }
     }
 }
@@ -350,32 +398,25 @@ __global__ __launch_bounds__(kBlock) void ln_affine_kernel(const chunk_t* x, con
     beta = params + T::kChunks;
     const int lane = threadIdx.x & 63;
     const int sub = lane % T::kLanes;
-    for (int64_t w = first_wave(); w * T::kRowsPerWave < rows; w += wave_stride()) {
+    const int64_t stride = wave_stride();
+    int64_t w = first_wave();
+    chunk_t v[K];
+    load_tile<C, K, H>(x, w, rows, lane, v);
+    for (; w * T::kRowsPerWave < rows; w += stride) {
         // re-read gamma/beta from LDS per row tile instead of letting the
         // compiler hoist 2*K widened chunks out of the loop into registers
         asm volatile("" ::: "memory");
-        const int64_t row = w * T::kRowsPerWave + lane / T::kLanes;
-        const bool live = row < rows;
-        const int64_t base = row * T::kChunks + sub;
-        chunk_t v[K];
-        zero(v);
-        if (live) {
-#pragma unroll
-            for (int k = 0; k < K; ++k) v[k] = load16<H>(x + base + k * T::kLanes);
-        }
         layer_norm_affine_lane<C, K>(v, gamma, beta, sub, eps);
-        if (live) {
-#pragma unroll
-            for (int k = 0; k < K; ++k) store16<H>(y + base + k * T::kLanes, v[k]);
-        }
+        store_tile<C, K, H>(y, w, rows, lane, v);
+        load_tile<C, K, H>(x, w + stride, rows, lane, v);
     }
 }
 
-template <int C, int K, class H>
+template <int C, int K, class H, bool kPrefetch>
 __global__ __launch_bounds__(kBlock) void add_ln_affine_kernel(const chunk_t* branch, const chunk_t* residual,
-                                                               const chunk_t* gamma, const chunk_t* beta,
-                                                               chunk_t* residual_out, chunk_t* y,
-                                                               int64_t rows, double eps) {
+                                                                 const chunk_t* gamma, const chunk_t* beta,
+                                                                 chunk_t* residual_out, chunk_t* y,
+                                                                 int64_t rows, double eps) {
     using T = Tile<C, K>;
     __shared__ chunk_t params[2 * T::kChunks];
     stage_params<C>(params, gamma, beta);
@@ -383,30 +424,31 @@ __global__ __launch_bounds__(kBlock) void add_ln_affine_kernel(const chunk_t* br
     beta = params + T::kChunks;
     const int lane = threadIdx.x & 63;
     const int sub = lane % T::kLanes;
-    for (int64_t w = first_wave(); w * T::kRowsPerWave < rows; w += wave_stride()) {
+    const int64_t stride = wave_stride();
+    int64_t w = first_wave();
+    chunk_t b[K], r[K];
+    load_tile<C, K, H>(branch, w, rows, lane, b);
+    load_tile<C, K, H>(residual, w, rows, lane, r);
+    for (; w * T::kRowsPerWave < rows; w += stride) {
+        chunk_t nb[K], nr[K];
+        if constexpr (kPrefetch) {
+            load_tile<C, K, H>(branch, w + stride, rows, lane, nb);
+            load_tile<C, K, H>(residual, w + stride, rows, lane, nr);
+        }
         asm volatile("" ::: "memory");  // as in ln_affine_kernel: no hoisting of gamma/beta
-        const int64_t row = w * T::kRowsPerWave + lane / T::kLanes;
-        const bool live = row < rows;
-        const int64_t base = row * T::kChunks + sub;
-        chunk_t b[K], r[K];
-        zero(b);
-        zero(r);
-        if (live) {
+        residual_add<K>(b, r);
+        store_tile<C, K, H>(residual_out, w, rows, lane, r);
+        layer_norm_affine_lane<C, K>(r, gamma, beta, sub, eps);
+        store_tile<C, K, H>(y, w, rows, lane, r);
+        if constexpr (kPrefetch) {
 #pragma unroll
             for (int k = 0; k < K; ++k) {
-                b[k] = load16<H>(branch + base + k * T::kLanes);
-                r[k] = load16<H>(residual + base + k * T::kLanes);
+                b[k] = nb[k];
+                r[k] = nr[k];
             }
-        }
-        residual_add<K>(b, r);
-        if (live) {
-#pragma unroll
-            for (int k = 0; k < K; ++k) store16<H>(residual_out + base + k * T::kLanes, r[k]);
-        }
-        layer_norm_affine_lane<C, K>(r, gamma, beta, sub, eps);
-        if (live) {
-#pragma unroll
-            for (int k = 0; k < K; ++k) store16<H>(y + base + k * T::kLanes, r[k]);
+        } else {
+            load_tile<C, K, H>(branch, w + stride, rows, lane, b);
+            load_tile<C, K, H>(residual, w + stride, rows, lane, r);
         }
     }
 }
@@ -414,31 +456,60 @@ __global__ __launch_bounds__(kBlock) void add_ln_affine_kernel(const chunk_t* br
 // Output-major gather: lane group j reads table[j] and, for a valid entry,
 // the whole source row; padding and out-of-range entries read nothing and
 // store +0.0 (LayerNorm of a zero row is exactly +0.0 as well).
-template <int C, int K, bool kNorm, class H>
+template <int C, int K, class H>
+__device__ __forceinline__ void load_gathered(const chunk_t* x, int64_t n_src, const int32_t* table,
+                                              int64_t n_out, int64_t w, int lane, chunk_t (&v)[K]) {
+    using T = Tile<C, K>;
+    const int64_t j = w * T::kRowsPerWave + lane / T::kLanes;
+    const int32_t t = j < n_out ? table[j] : -1;
+    zero(v);
+    if (t >= 0 && static_cast<int64_t>(t) < n_src) {
+        const int64_t src = static_cast<int64_t>(t) * T::kChunks + lane % T::kLanes;
+#pragma unroll
+        for (int k = 0; k < K; ++k) v[k] = load16<H>(x + src + k * T::kLanes);
+    }
+}
+
+template <int C, int K, bool kNorm, class H, bool kPrefetch>
 __global__ __launch_bounds__(kBlock) void gather_kernel(const chunk_t* __restrict__ x, int64_t n_src,
                                                         const int32_t* __restrict__ table,
                                                         int64_t n_out, chunk_t* __restrict__ out,
                                                         double eps) {
     using T = Tile<C, K>;
     const int lane = threadIdx.x & 63;
-    const int sub = lane % T::kLanes;
-    for (int64_t w = first_wave(); w * T::kRowsPerWave < n_out; w += wave_stride()) {
-        const int64_t j = w * T::kRowsPerWave + lane / T::kLanes;
-        const bool live = j < n_out;
-        const int32_t t = live ? table[j] : -1;
-        const bool valid = t >= 0 && static_cast<int64_t>(t) < n_src;
-        const int64_t src = static_cast<int64_t>(t) * T::kChunks + sub;
+    if constexpr (kPrefetch) {
+        const int64_t stride = wave_stride();
+        int64_t w = first_wave();
         chunk_t v[K];
-        zero(v);
-        if (valid) {
+        load_gathered<C, K, H>(x, n_src, table, n_out, w, lane, v);
+        for (; w * T::kRowsPerWave < n_out; w += stride) {
+            chunk_t next[K];
+            load_gathered<C, K, H>(x, n_src, table, n_out, w + stride, lane, next);
+            if constexpr (kNorm) layer_norm_lane<C, K>(v, eps);
+            store_tile<C, K, H>(out, w, n_out, lane, v);
 #pragma unroll
-            for (int k = 0; k < K; ++k) v[k] = load16<H>(x + src + k * T::kLanes);
+            for (int k = 0; k < K; ++k) v[k] = next[k];
         }
-        if constexpr (kNorm) layer_norm_lane<C, K>(v, eps);
-        if (live) {
-            const int64_t dst = j * T::kChunks + sub;
+    } else {
+        const int sub = lane % T::kLanes;
+        for (int64_t w = first_wave(); w * T::kRowsPerWave < n_out; w += wave_stride()) {
+            const int64_t j = w * T::kRowsPerWave + lane / T::kLanes;
+            const bool live = j < n_out;
+            const int32_t t = live ? table[j] : -1;
+            const bool valid = t >= 0 && static_cast<int64_t>(t) < n_src;
+            const int64_t src = static_cast<int64_t>(t) * T::kChunks + sub;
+            chunk_t v[K];
+            zero(v);
+            if (valid) {
 #pragma unroll
-            for (int k = 0; k < K; ++k) store16<H>(out + dst + k * T::kLanes, v[k]);
+                for (int k = 0; k < K; ++k) v[k] = load16<H>(x + src + k * T::kLanes);
+            }
+            if constexpr (kNorm) layer_norm_lane<C, K>(v, eps);
+            if (live) {
+                const int64_t dst = j * T::kChunks + sub;
+#pragma unroll
+                for (int k = 0; k < K; ++k) store16<H>(out + dst + k * T::kLanes, v[k]);
+            }
         }
     }
 }
@@ -447,43 +518,63 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(const chunk_t* __restric
 // its branch from window row idx[i] (the inverse table), adds the residual,
 // writes the rounded sum, and normalises it. An index outside [0, n_win) gives
 // a zero branch. residual_out and y may alias residual (row i is read and
-// written by the same lanes).
-template <int C, int K, class H>
+// written by the same lanes; a prefetched tile holds other rows); neither may
+// overlap win, whose rows a prefetch may read after another row was written.
+template <int C, int K, class H, bool kPrefetch>
 __global__ __launch_bounds__(kBlock) void reverse_add_ln_kernel(
     const chunk_t* __restrict__ win, int64_t n_win, const int32_t* __restrict__ idx,
     const chunk_t* residual, chunk_t* residual_out, chunk_t* y, int64_t rows, double eps) {
     using T = Tile<C, K>;
     const int lane = threadIdx.x & 63;
-    const int sub = lane % T::kLanes;
-    for (int64_t w = first_wave(); w * T::kRowsPerWave < rows; w += wave_stride()) {
-        const int64_t row = w * T::kRowsPerWave + lane / T::kLanes;
-        const bool live = row < rows;
-        const int32_t t = live ? idx[row] : -1;
-        const bool valid = t >= 0 && static_cast<int64_t>(t) < n_win;
-        const int64_t base = row * T::kChunks + sub;
-        const int64_t src = static_cast<int64_t>(t) * T::kChunks + sub;
-        chunk_t b[K], r[K];
-        zero(b);
-        zero(r);
-        if (valid) {
-#pragma unroll
-            for (int k = 0; k < K; ++k) b[k] = load16<H>(win + src + k * T::kLanes);
-        }
-        if (live) {
-#pragma unroll
-            for (int k = 0; k < K; ++k) r[k] = load16<H>(residual + base + k * T::kLanes);
+    const int64_t stride = wave_stride();
+    int64_t w = first_wave();
+    chunk_t b[K], r[K];
+    load_gathered<C, K, H>(win, n_win, idx, rows, w, lane, b);
+    load_tile<C, K, H>(residual, w, rows, lane, r);
+    for (; w * T::kRowsPerWave < rows; w += stride) {
+        chunk_t nb[K], nr[K];
+        if constexpr (kPrefetch) {
+            load_gathered<C, K, H>(win, n_win, idx, rows, w + stride, lane, nb);
+            load_tile<C, K, H>(residual, w + stride, rows, lane, nr);
         }
         residual_add<K>(b, r);
-        if (live) {
-#pragma unroll
-            for (int k = 0; k < K; ++k) store16<H>(residual_out + base + k * T::kLanes, r[k]);
-        }
+        store_tile<C, K, H>(residual_out, w, rows, lane, r);
         layer_norm_lane<C, K>(r, eps);
-        if (live) {
+        store_tile<C, K, H>(y, w, rows, lane, r);
+        if constexpr (kPrefetch) {
 #pragma unroll
-            for (int k = 0; k < K; ++k) store16<H>(y + base + k * T::kLanes, r[k]);
+            for (int k = 0; k < K; ++k) {
+                b[k] = nb[k];
+                r[k] = nr[k];
+            }
+        } else {
+            load_gathered<C, K, H>(win, n_win, idx, rows, w + stride, lane, b);
+            load_tile<C, K, H>(residual, w + stride, rows, lane, r);
         }
     }
+}
+
+// Branch and residual chunks of the source row of gathered row j (zeros and -1
+// for padding or an out-of-range entry); returns the source row or -1.
+template <int C, int K, class H>
+__device__ __forceinline__ int32_t load_pair(const chunk_t* branch, const chunk_t* residual, int64_t n_src,
+                                             const int32_t* table, int64_t n_out, int64_t w, int lane,
+                                             chunk_t (&b)[K], chunk_t (&r)[K]) {
+    using T = Tile<C, K>;
+    const int64_t j = w * T::kRowsPerWave + lane / T::kLanes;
+    int32_t t = j < n_out ? table[j] : -1;
+    if (!(t >= 0 && static_cast<int64_t>(t) < n_src)) t = -1;
+    zero(b);
+    zero(r);
+    if (t >= 0) {
+        const int64_t src = static_cast<int64_t>(t) * T::kChunks + lane % T::kLanes;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            b[k] = load16<H>(branch + src + k * T::kLanes);
+            r[k] = load16<H>(residual + src + k * T::kLanes);
+        }
+    }
+    return t;
 }
 
 // Residual add + LayerNorm + window gather, output-major: gathered row j reads
@@ -491,40 +582,41 @@ __global__ __launch_bounds__(kBlock) void reverse_add_ln_kernel(
 // residual_out[t] and its LayerNorm to out[j]; padding rows store +0.0 and
 // touch no token. With a table whose valid entries are distinct (as built by
 // window_index_kernel) every token row is read and written by exactly one lane
-// group, so residual_out may alias residual or branch.
-template <int C, int K, class H>
+// group, and a prefetched tile reads other tokens than the one being written,
+// so residual_out may alias residual or branch.
+template <int C, int K, class H, bool kPrefetch>
 __global__ __launch_bounds__(kBlock) void add_norm_gather_kernel(
     const chunk_t* branch, const chunk_t* residual, chunk_t* residual_out, int64_t n_src,
     const int32_t* __restrict__ table, int64_t n_out, chunk_t* __restrict__ out, double eps) {
     using T = Tile<C, K>;
     const int lane = threadIdx.x & 63;
     const int sub = lane % T::kLanes;
-    for (int64_t w = first_wave(); w * T::kRowsPerWave < n_out; w += wave_stride()) {
-        const int64_t j = w * T::kRowsPerWave + lane / T::kLanes;
-        const bool live = j < n_out;
-        const int32_t t = live ? table[j] : -1;
-        const bool valid = t >= 0 && static_cast<int64_t>(t) < n_src;
-        const int64_t src = static_cast<int64_t>(t) * T::kChunks + sub;
-        chunk_t b[K], r[K];
-        zero(b);
-        zero(r);
-        if (valid) {
-#pragma unroll
-            for (int k = 0; k < K; ++k) {
-                b[k] = load16<H>(branch + src + k * T::kLanes);
-                r[k] = load16<H>(residual + src + k * T::kLanes);
-            }
-        }
+    const int64_t stride = wave_stride();
+    int64_t w = first_wave();
+    chunk_t b[K], r[K];
+    int32_t t = load_pair<C, K, H>(branch, residual, n_src, table, n_out, w, lane, b, r);
+    for (; w * T::kRowsPerWave < n_out; w += stride) {
+        chunk_t nb[K], nr[K];
+        int32_t nt = -1;
+        if constexpr (kPrefetch)
+            nt = load_pair<C, K, H>(branch, residual, n_src, table, n_out, w + stride, lane, nb, nr);
         residual_add<K>(b, r);
-        if (valid) {
+        if (t >= 0) {
+            const int64_t src = static_cast<int64_t>(t) * T::kChunks + sub;
 #pragma unroll
             for (int k = 0; k < K; ++k) store16<H>(residual_out + src + k * T::kLanes, r[k]);
         }
         layer_norm_lane<C, K>(r, eps);
-        if (live) {
-            const int64_t dst = j * T::kChunks + sub;
+        store_tile<C, K, H>(out, w, n_out, lane, r);
+        if constexpr (kPrefetch) {
 #pragma unroll
-            for (int k = 0; k < K; ++k) store16<H>(out + dst + k * T::kLanes, r[k]);
+            for (int k = 0; k < K; ++k) {
+                b[k] = nb[k];
+                r[k] = nr[k];
+            }
+            t = nt;
+        } else {
+            t = load_pair<C, K, H>(branch, residual, n_src, table, n_out, w + stride, lane, b, r);
         }
     }
 }
@@ -635,8 +727,9 @@ __global__ __launch_bounds__(kBlock) void bias_gelu_kernel(const f32x4_t* x, con
 // Every kernel streams its inputs once and never re-reads its outputs, so all
 // loads and stores carry the non-temporal hint; on cold data that beat plain
 // and store-only-hinted accesses for every kernel. The grid is one tile per
-// wave, except the C = 384 norm-gather, which is capped at 4 workgroups per
-// compute unit with each wave looping over tiles.
+// wave unless the table of Launch entries below says otherwise. (K = 3 at
+// C = 384, 16 lanes per row, measured -2% on the gathers and +5% / +16% on
+// ln_fixed / ln_affine: not taken.)
 enum class Op { kLn, kAddLn, kGather, kNormGather, kReverseAddLn, kAddNormGather, kLnAffine, kAddLnAffine };
 
 template <int C> struct Width;
@@ -648,8 +741,43 @@ template <> struct Width<768> { static constexpr int K = 6; };
 
 using Streaming = Hints<true, true>;
 
-template <int C, Op O> struct Launch { using H = Streaming; static constexpr int kBlocksPerCu = 0; };
-template <> struct Launch<384, Op::kNormGather> { using H = Streaming; static constexpr int kBlocksPerCu = 4; };
+// Per (width, op): kBlocksPerCu caps the grid at that many workgroups per
+// compute unit (0 = one tile per wave); kPrefetch selects the software-pipelined
+// row loop (the next tile's loads issued before the current tile is
+// normalised). Each entry was measured against the alternatives on cold
+// buffers, in interleaved runs on one MI355X:
+//  * C = 384: the pipelined single-input kernels hold 150-160 VGPRs (3 waves
+//    per SIMD) and the two-input ones 190-194 (2 waves); a cap that fills
+//    exactly those slots lets each wave take 1.3-2.3 tiles and normalise one
+//    while the next loads: ln_fixed -11%, norm_gather -10%, add_ln -4%,
+//    window_reverse_add_ln -4%, add_ln_affine -6%. ln_affine gains 9% from the
+//    cap alone and add_norm_gather 1% (both lose with the pipeline).
+//  * C = 192, one tile per wave: the pipelined form of ln_fixed, add_ln and the
+//    fused residual kernels issues the tile's loads ahead of the loop test and
+//    measured 2-4% faster; the gathers and ln_affine are fastest as they are.
+//  * C = 768 and everything else: the default.
+template <int C, Op O> struct Launch {
+    using H = Streaming;
+    static constexpr int kBlocksPerCu = 0;
+    static constexpr bool kPrefetch = false;
+};
+template <int Cap, bool Prefetch> struct Tuned {
+    using H = Streaming;
+    static constexpr int kBlocksPerCu = Cap;
+    static constexpr bool kPrefetch = Prefetch;
+};
+template <> struct Launch<192, Op::kLn> : Tuned<0, true> {};
+template <> struct Launch<192, Op::kAddLn> : Tuned<0, true> {};
+template <> struct Launch<192, Op::kReverseAddLn> : Tuned<0, true> {};
+template <> struct Launch<192, Op::kAddNormGather> : Tuned<0, true> {};
+template <> struct Launch<192, Op::kAddLnAffine> : Tuned<0, true> {};
+template <> struct Launch<384, Op::kLn> : Tuned<3, true> {};
+template <> struct Launch<384, Op::kNormGather> : Tuned<3, true> {};
+template <> struct Launch<384, Op::kAddLn> : Tuned<2, true> {};
+template <> struct Launch<384, Op::kReverseAddLn> : Tuned<2, true> {};
+template <> struct Launch<384, Op::kAddLnAffine> : Tuned<2, true> {};
+template <> struct Launch<384, Op::kLnAffine> : Tuned<3, false> {};
+template <> struct Launch<384, Op::kAddNormGather> : Tuned<2, false> {};
 
 
 // Compute units of the device, queried on first use (0 = not yet known). Only
@@ -686,7 +814,7 @@ unsigned grid_for(int64_t rows) {
 template <int C>
 hipError_t ln_fixed_c(const void* x, void* y, int64_t rows, double eps, hipStream_t s) {
     using L = Launch<C, Op::kLn>;
-    ln_fixed_kernel<C, Width<C>::K, typename L::H><<<grid_for<C, Op::kLn>(rows), kBlock, 0, s>>>(
+    ln_fixed_kernel<C, Width<C>::K, typename L::H, L::kPrefetch><<<grid_for<C, Op::kLn>(rows), kBlock, 0, s>>>(
         static_cast<const chunk_t*>(x), static_cast<chunk_t*>(y), rows, eps);
     return hipGetLastError();
 }
@@ -695,7 +823,7 @@ template <int C>
 hipError_t add_ln_c(const void* b, const void* r, void* ro, void* y, int64_t rows, double eps,
                     hipStream_t s) {
     using L = Launch<C, Op::kAddLn>;
-    add_ln_kernel<C, Width<C>::K, typename L::H><<<grid_for<C, Op::kAddLn>(rows), kBlock, 0, s>>>(
+    add_ln_kernel<C, Width<C>::K, typename L::H, L::kPrefetch><<<grid_for<C, Op::kAddLn>(rows), kBlock, 0, s>>>(
         static_cast<const chunk_t*>(b), static_cast<const chunk_t*>(r), static_cast<chunk_t*>(ro),
         static_cast<chunk_t*>(y), rows, eps);
     return hipGetLastError();
@@ -706,7 +834,7 @@ hipError_t gather_c(const void* x, int64_t n_src, const int32_t* table, int64_t 
                     void* out, hipStream_t s) {
     constexpr Op O = kNorm ? Op::kNormGather : Op::kGather;
     using L = Launch<C, O>;
-    gather_kernel<C, Width<C>::K, kNorm, typename L::H><<<grid_for<C, O>(n_out), kBlock, 0, s>>>(
+    gather_kernel<C, Width<C>::K, kNorm, typename L::H, L::kPrefetch><<<grid_for<C, O>(n_out), kBlock, 0, s>>>(
         static_cast<const chunk_t*>(x), n_src, table, n_out, static_cast<chunk_t*>(out), eps);
     return hipGetLastError();
 }
@@ -761,7 +889,7 @@ template <int C>
 hipError_t reverse_add_ln_c(const void* win, int64_t n_win, const int32_t* idx, const void* r, void* ro,
                             void* y, int64_t rows, double eps, hipStream_t s) {
     using L = Launch<C, Op::kReverseAddLn>;
-    reverse_add_ln_kernel<C, Width<C>::K, typename L::H>
+    reverse_add_ln_kernel<C, Width<C>::K, typename L::H, L::kPrefetch>
         <<<grid_for<C, Op::kReverseAddLn>(rows), kBlock, 0, s>>>(
             static_cast<const chunk_t*>(win), n_win, idx, static_cast<const chunk_t*>(r),
             static_cast<chunk_t*>(ro), static_cast<chunk_t*>(y), rows, eps);
@@ -778,7 +906,7 @@ template <int C>
 hipError_t add_norm_gather_c(const void* b, const void* r, void* ro, int64_t n_src, const int32_t* table,
                              int64_t n_out, double eps, void* out, hipStream_t s) {
     using L = Launch<C, Op::kAddNormGather>;
-    add_norm_gather_kernel<C, Width<C>::K, typename L::H>
+    add_norm_gather_kernel<C, Width<C>::K, typename L::H, L::kPrefetch>
         <<<grid_for<C, Op::kAddNormGather>(n_out), kBlock, 0, s>>>(
             static_cast<const chunk_t*>(b), static_cast<const chunk_t*>(r), static_cast<chunk_t*>(ro),
             n_src, table, n_out, static_cast<chunk_t*>(out), eps);
@@ -810,7 +938,7 @@ template <int C>
 hipError_t add_ln_affine_c(const void* br, const void* r, const void* g, const void* b, void* ro, void* y,
                            int64_t rows, double eps, hipStream_t s) {
     using L = Launch<C, Op::kAddLnAffine>;
-    add_ln_affine_kernel<C, Width<C>::K, typename L::H>
+    add_ln_affine_kernel<C, Width<C>::K, typename L::H, L::kPrefetch>
         <<<grid_for<C, Op::kAddLnAffine>(rows), kBlock, 0, s>>>(
             static_cast<const chunk_t*>(br), static_cast<const chunk_t*>(r), static_cast<const chunk_t*>(g),
             static_cast<const chunk_t*>(b), static_cast<chunk_t*>(ro), static_cast<chunk_t*>(y), rows, eps);
