@@ -565,6 +565,8 @@ def main(argv=None):
             "buffer_sets": args.sets, "device": props.name,
             "arch": getattr(props, "gcnArchName", "?"), "cus": props.multi_processor_count,
             "memory": memory_attributes(dev.index or 0),
+            "versions": {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
+                         "python": sys.version.split()[0], "numpy": np.__version__},
             "seeds": {"level1": 1, "level2": 2, "patch_merge_rows": 11, "patch_merge_values": 12,
                       "replay_streams": 4, "replay_branch_of_block_b": "4 + b",
                       "bias_gelu_torch_cpu_generator": 20260716},
