@@ -145,9 +145,12 @@ LWG_EXPORT int64_t lwg_window_token_count(int32_t Z, int32_t H, int32_t W, int32
                                           int32_t ww) {
     const int64_t zp = padded(Z, wz), hp = padded(H, wh), wp = padded(W, ww);
     if (zp < 0 || hp < 0 || wp < 0) return -1;
-    // each padded extent is below 2^32, so check the product stepwise
+    if (zp == 0 || hp == 0 || wp == 0) return 0;
+    // a padded extent can reach 2^32 - 2; bound every factor and partial product
+    // by 2^31 - 1 before the next multiply, so no product leaves int64
+    if (zp > INT32_MAX || hp > INT32_MAX || wp > INT32_MAX) return -1;
     const int64_t zh = zp * hp;
-    if (zh > INT32_MAX || (wp != 0 && zh > INT32_MAX / wp)) return -1;
+    if (zh > INT32_MAX) return -1;
     const int64_t n = zh * wp;
     return n > INT32_MAX ? -1 : n;
 }
@@ -165,9 +168,11 @@ int32_t window_geometry(const char* fn, int32_t Z, int32_t H, int32_t W, int32_t
         return fail(LWG_ERR_INVALID_ARGUMENT, "%s: window extents must be >= 1 (got %d,%d,%d)", fn, wz, wh, ww);
     if (sz < 0 || sh < 0 || sw < 0)
         return fail(LWG_ERR_INVALID_ARGUMENT, "%s: shifts must be >= 0 (got %d,%d,%d)", fn, sz, sh, sw);
-    const int64_t tokens = static_cast<int64_t>(Z) * H * W;
-    if (tokens > INT32_MAX)
+    // Z*H < 2^62; bound it before multiplying by W so the product stays in int64
+    const int64_t zh = static_cast<int64_t>(Z) * H;
+    if (W != 0 && (zh > INT32_MAX || zh * W > INT32_MAX))
         return fail(LWG_ERR_INVALID_ARGUMENT, "%s: grid holds more than 2^31-1 tokens", fn);
+    const int64_t tokens = zh * W;
     const int64_t m = lwg_window_token_count(Z, H, W, wz, wh, ww);
     if (m < 0)
         return fail(LWG_ERR_INVALID_ARGUMENT, "%s: padded grid holds more than 2^31-1 rows", fn);

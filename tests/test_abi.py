@@ -275,3 +275,17 @@ def test_header_is_strict_c99(tmp_path):
     res = subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-fsyntax-only",
                           "-I", os.path.join(ROOT, "include"), str(src)], capture_output=True, text=True)
     assert res.returncode == 0, res.stderr
+
+
+def test_huge_grids_are_refused_without_overflow():
+    """Grid products past 2^63 (a padded extent can reach 2^32 - 2) are refused,
+    not wrapped: the token count is -1 and both table builders refuse."""
+    lib = _lib.load()
+    big = 2**31 - 1
+    assert lib.lwg_window_token_count(big, big, big, 1, 1, 1) == -1
+    assert lib.lwg_window_token_count(big, big, 1, big - 1, big - 1, 1) == -1
+    assert lib.lwg_window_token_count(0, big, big, 1, 1, 1) == 0
+    st = lib.lwg_window_index_build(big, big, big, 1, 1, 1, 0, 0, 0, ctypes.c_void_p(0x1000), 1, None)
+    assert st == _lib.LWG_ERR_INVALID_ARGUMENT
+    st = lib.lwg_window_inverse_build(big, big, big, 2, 6, 12, 0, 0, 0, ctypes.c_void_p(0x1000), 1, None)
+    assert st == _lib.LWG_ERR_INVALID_ARGUMENT
