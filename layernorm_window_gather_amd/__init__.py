@@ -9,7 +9,7 @@ refused.
 
 Operations (page "Pangu-Weather inference optimisation on Hygon BW1000
 (gfx936)", sections 3-5):
-  ln_fixed(x)                        LayerNorm of rows of width 192/384, no affine
+  ln_fixed(x)                        LayerNorm of rows of width 192/384/768, no affine
   add_ln(branch, residual)           (FP16(residual + branch), LayerNorm of it)
   window_token_count(grid, window)   rows of the padded, windowed tensor
   window_index_build(grid, window, shift)   INT32 table built on the device
@@ -95,7 +95,7 @@ def _out_like(out, shape, device, name):
 
 
 def ln_fixed(x: torch.Tensor, eps: float = EPS, out: torch.Tensor = None) -> torch.Tensor:
-    """LayerNorm over the last dimension (192 or 384) without affine; ``out`` may be ``x``."""
+    """LayerNorm over the last dimension (192, 384 or 768) without affine; ``out`` may be ``x``."""
     rows = _rows(x, "x")
     y = _out_like(out, x.shape, x.device, "out")
     lib = _lib.load()
