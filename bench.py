@@ -217,6 +217,79 @@ def parity_gate(lwg, torch, sets, host, levels, m_of):
     return True
 
 
+def next_ops_gate(lwg, torch, dev, host, levels):
+    """Sampled parity of the ops reported per kernel but not in the step (the
+    table inverse, the fused residual kernels, the affine LayerNorms, width 768
+    and bias_gelu), one call each on seeded inputs, before any timing. Inputs
+    come from workloads or the oracle, never from a HIP output."""
+    import oracle
+    rng = np.random.default_rng(321)
+
+    def close(name, got, ref):
+        d = np.abs(got.astype(np.float64) - ref.astype(np.float64))
+        if not (d.max() <= 2e-3 and d.mean() <= 1e-4):
+            raise SystemExit(f"parity gate failed: {name}")
+
+    def exact(name, got, ref):
+        if not np.array_equal(np.asarray(got).view(np.uint16), np.asarray(ref).view(np.uint16)):
+            raise SystemExit(f"parity gate failed: {name}")
+
+    for lv in levels:
+        x, residual = host[lv.name]
+        n, c = lv.tokens, lv.channels
+        table = oracle.window_index_table(lv.grid, WINDOW, SHIFT)
+        inv = oracle.window_inverse_table(lv.grid, WINDOW, SHIFT)
+        m = table.shape[0]
+        rows = np.unique(np.concatenate([rng.choice(n, 1024, replace=False), [0, n - 1]]))
+        jrows = np.unique(np.concatenate([rng.choice(m, 1024, replace=False), [m - 1]]))
+        tx, tr = torch.from_numpy(x).to(dev), torch.from_numpy(residual).to(dev)
+        tinv = lwg.window_inverse_build(lv.grid, WINDOW, SHIFT, device=dev)
+        if not np.array_equal(tinv.cpu().numpy(), inv):
+            raise SystemExit(f"parity gate: inverse table differs at {lv.name}")
+        win = workloads.normal_rows(700 + c, m, c)
+        r, y = lwg.window_reverse_add_ln(torch.from_numpy(win).to(dev), tinv, tr)
+        r_ref, y_ref = oracle.add_ln(win[inv[rows]], residual[rows])
+        exact(f"window_reverse_add_ln residual at {lv.name}", r.cpu().numpy()[rows], r_ref)
+        close(f"window_reverse_add_ln at {lv.name}", y.cpu().numpy()[rows], y_ref)
+        ttab = lwg.window_table(lv.grid, WINDOW, SHIFT, device=dev)
+        r, g = lwg.add_norm_gather(tx, tr, ttab)
+        exact(f"add_norm_gather residual at {lv.name}", r.cpu().numpy()[rows], oracle.residual_sum(residual[rows], x[rows]))
+        t = table[jrows]
+        ref = np.zeros((jrows.size, c), np.float16)
+        ref[t >= 0] = oracle.layer_norm(oracle.residual_sum(residual[t[t >= 0]], x[t[t >= 0]]))
+        close(f"add_norm_gather at {lv.name}", g.cpu().numpy()[jrows], ref)
+        gamma = np.linspace(0.5, 1.5, c).astype(np.float16)
+        beta = np.linspace(-0.25, 0.25, c).astype(np.float16)
+        tg, tb = torch.from_numpy(gamma).to(dev), torch.from_numpy(beta).to(dev)
+        close(f"ln_affine at {lv.name}", lwg.ln_affine(tx, tg, tb).cpu().numpy()[rows],
+              oracle.layer_norm_affine(x[rows], gamma, beta))
+        r, y = lwg.add_ln_affine(tx, tr, tg, tb)
+        r_ref, y_ref = oracle.add_ln_affine(x[rows], residual[rows], gamma, beta)
+        exact(f"add_ln_affine residual at {lv.name}", r.cpu().numpy()[rows], r_ref)
+        close(f"add_ln_affine at {lv.name}", y.cpu().numpy()[rows], y_ref)
+    # width 768 (patch merge) and the float32 bias + GELU
+    nc, off = workloads.stress_row_classes(11, PATCH_MERGE.tokens)
+    xm = workloads.mixed_rows(12, PATCH_MERGE.tokens, PATCH_MERGE.channels, nc, off)
+    rows = np.unique(np.concatenate([rng.choice(PATCH_MERGE.tokens, 1024, replace=False), nc[:64], off[:64]]))
+    txm = torch.from_numpy(xm).to(dev)
+    close("ln_fixed at width 768", lwg.ln_fixed(txm).cpu().numpy()[rows], oracle.layer_norm(xm[rows]))
+    gamma = np.linspace(0.5, 1.5, 768).astype(np.float16)
+    beta = np.linspace(-0.25, 0.25, 768).astype(np.float16)
+    close("ln_affine at width 768",
+          lwg.ln_affine(txm, torch.from_numpy(gamma).to(dev), torch.from_numpy(beta).to(dev)).cpu().numpy()[rows],
+          oracle.layer_norm_affine(xm[rows], gamma, beta))
+    grng = np.random.default_rng(20260716)
+    xg = grng.normal(0.0, 1.0, size=GELU_SHAPES[-1]).astype(np.float32)
+    bg = grng.normal(0.0, 1.0, size=GELU_SHAPES[-1][1]).astype(np.float32)
+    grows = rng.choice(xg.shape[0], 256, replace=False)
+    got = lwg.bias_gelu(torch.from_numpy(xg).to(dev), torch.from_numpy(bg).to(dev)).cpu().numpy()[grows]
+    ref = oracle.bias_gelu(xg[grows], bg).astype(np.float64)
+    if not np.all(np.abs(got.astype(np.float64) - ref) <= 2e-5 + 2e-5 * np.abs(ref)):
+        raise SystemExit("parity gate failed: bias_gelu")
+    torch.cuda.synchronize()
+    return True
+
+
 def memory_attributes(dev_index: int):
     """The device's reported memory clock (kHz) and bus width (bits), read with
     hipDeviceGetAttribute, and the figure clock x bus width x 2 transfers per
@@ -353,6 +426,8 @@ def main(argv=None):
     torch.cuda.synchronize()
 
     parity_gate(lwg, torch, sets, host, levels, m_of)
+    if args.only is None:
+        next_ops_gate(lwg, torch, dev, host, levels)
 
     bytes_of = {(lv.name, op): algorithmic_bytes(op, lv.tokens, m_of[lv.name], lv.channels)
                 for lv in levels for op in OPS + NEXT_OPS}
@@ -584,6 +659,7 @@ def main(argv=None):
             "timing": f"HIP events around {args.kernel_reps} back-to-back launches on the launch stream, "
                       "median of 5 runs, buffers rotated so each is reused >= 1.25 GiB of traffic later",
         },
+        "parity_gate": "passed: sampled outputs of every reported op against the oracle, before timing",
         "kernels": kernels,
         "replay": replay,
     }
