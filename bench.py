@@ -278,9 +278,7 @@ def next_ops_gate(lwg, torch, dev, host, levels):
     close("ln_affine at width 768",
           lwg.ln_affine(txm, torch.from_numpy(gamma).to(dev), torch.from_numpy(beta).to(dev)).cpu().numpy()[rows],
           oracle.layer_norm_affine(xm[rows], gamma, beta))
-    grng = np.random.default_rng(20260716)
-    xg = grng.normal(0.0, 1.0, size=GELU_SHAPES[-1]).astype(np.float32)
-    bg = grng.normal(0.0, 1.0, size=GELU_SHAPES[-1][1]).astype(np.float32)
+    xg, bg = workloads.gelu_inputs(20260716, *GELU_SHAPES[-1])
     grows = rng.choice(xg.shape[0], 256, replace=False)
     got = lwg.bias_gelu(torch.from_numpy(xg).to(dev), torch.from_numpy(bg).to(dev)).cpu().numpy()[grows]
     ref = oracle.bias_gelu(xg[grows], bg).astype(np.float64)
@@ -445,9 +443,9 @@ def main(argv=None):
                 for i in range(args.warmup + args.steps):
                     calls[i % len(calls)]()
         if args.only == "all":
-            gen = torch.Generator(device="cpu").manual_seed(1)
             for rows, cols in GELU_SHAPES[-1:]:
-                xg, bg = torch.randn(rows, cols, generator=gen).to(dev), torch.randn(cols, generator=gen).to(dev)
+                xh, bh = workloads.gelu_inputs(20260716, rows, cols)
+                xg, bg = torch.from_numpy(xh).to(dev), torch.from_numpy(bh).to(dev)
                 call = lwg.prepare("bias_gelu", xg, bg, torch.empty_like(xg))
                 for _ in range(args.warmup + args.steps):
                     call()
@@ -544,9 +542,9 @@ def main(argv=None):
     for rows, cols in GELU_SHAPES:
         nb = 2 * rows * cols * 4 + cols * 4
         count = min(64, max(3, -(-COLD_BYTES // nb) + 1))
-        gen = torch.Generator(device="cpu").manual_seed(20260716)
-        xs = [torch.randn(rows, cols, generator=gen).to(dev) for _ in range(1)]
-        bias = torch.randn(cols, generator=gen).to(dev)
+        xh, bh = workloads.gelu_inputs(20260716, rows, cols)
+        xs = [torch.from_numpy(xh).to(dev)]
+        bias = torch.from_numpy(bh).to(dev)
         pool = []
         for _ in range(count):
             xi = xs[0].clone()
@@ -644,7 +642,7 @@ def main(argv=None):
                          "python": sys.version.split()[0], "numpy": np.__version__},
             "seeds": {"level1": 1, "level2": 2, "patch_merge_rows": 11, "patch_merge_values": 12,
                       "replay_streams": 4, "replay_branch_of_block_b": "4 + b",
-                      "bias_gelu_torch_cpu_generator": 20260716},
+                      "bias_gelu": 20260716},
         },
         "roofline": {
             "kernel": "add_ln@level1",

@@ -6,6 +6,7 @@ import numpy as np
 import pytest
 
 import oracle
+import workloads
 
 from parity_helpers import host, to_dev
 
@@ -31,9 +32,7 @@ def _close(got, ref, label):
 
 @pytest.mark.parametrize("rows,cols", [(1024, 768), (4096, 1024), (8192, 2048), (1, 4), (3, 12), (257, 96)])
 def test_bias_gelu_matches_oracle(dev, rows, cols):
-    rng = np.random.default_rng(rows * 7 + cols)
-    x = rng.normal(0, 1, size=(rows, cols)).astype(np.float32)
-    b = rng.normal(0, 1, size=cols).astype(np.float32)
+    x, b = workloads.gelu_inputs(rows * 7 + cols, rows, cols)
     y = host(lwg.bias_gelu(to_dev(x, dev), to_dev(b, dev)))
     _close(y, oracle.bias_gelu(x, b), f"bias_gelu {rows}x{cols}")
 
@@ -54,9 +53,8 @@ def test_bias_gelu_edge_values_and_in_place(dev):
 
 def test_bias_gelu_matches_the_pages_eager_reference(dev):
     # the page's reference: torch's float32 gelu(input + bias, approximate="tanh")
-    g = torch.Generator(device="cpu").manual_seed(20260716)
-    x = torch.randn(4096, 1024, generator=g).to(dev)
-    b = torch.randn(1024, generator=g).to(dev)
+    xh, bh = workloads.gelu_inputs(20260716, 4096, 1024)
+    x, b = to_dev(xh, dev), to_dev(bh, dev)
     ref = torch.nn.functional.gelu(x + b, approximate="tanh")
     assert torch.allclose(lwg.bias_gelu(x, b), ref, rtol=RTOL, atol=ATOL)
 

@@ -30,7 +30,7 @@ REPLAYS = 4
 def inputs(seed, n, m, C):
     """Host inputs of one replay: fp16 rows for x, branch, residual and the
     window-major attention output, float32 rows and bias for the GELU."""
-    rng = np.random.default_rng(seed)
+    xf, bias = workloads.gelu_inputs(seed + 6, 96, C)
     return {
         "x": workloads.normal_rows(seed, n, C, mean=0.3, std=2.0),
         "branch": workloads.normal_rows(seed + 1, n, C),
@@ -38,8 +38,8 @@ def inputs(seed, n, m, C):
         "win": workloads.normal_rows(seed + 3, m, C),
         "gamma": workloads.normal_rows(seed + 4, 1, C)[0],
         "beta": workloads.normal_rows(seed + 5, 1, C, std=0.1)[0],
-        "xf": rng.normal(0.0, 1.0, size=(96, C)).astype(np.float32),
-        "bias": rng.normal(0.0, 1.0, size=C).astype(np.float32),
+        "xf": xf,
+        "bias": bias,
     }
 
 

@@ -97,13 +97,7 @@ def _golden_pairs():
 
 @pytest.mark.parametrize("C", [192, 384])
 def test_add_ln_residual_bit_exact_on_all_kinds_of_pairs(dev, C):
-    rng = np.random.default_rng(21)
-    rows = 700
-    res = rng.integers(0, 1 << 16, size=(rows, C), dtype=np.uint32).astype(np.uint16)
-    br = rng.integers(0, 1 << 16, size=(rows, C), dtype=np.uint32).astype(np.uint16)
-    # half the rows: close magnitudes of opposite sign (cancellation, subnormal results)
-    br[::2] = (res[::2].astype(np.int32) ^ 0x8000) + rng.integers(-3, 4, size=(rows // 2, C))
-    res, br = res.view(np.float16), br.view(np.float16)
+    res, br = workloads.fp16_bit_pattern_pairs(21, 700, C)
     gr, gb = _golden_pairs()
     res[0, : gr.size], br[0, : gb.size] = gr, gb
     r, y = lwg.add_ln(to_dev(br, dev), to_dev(res, dev))
@@ -211,13 +205,8 @@ def test_window_gather_bit_exact(dev, C, grid, shift):
 
 @pytest.mark.parametrize("C", [192, 384])
 def test_gather_out_of_range_entries_are_zero_rows(dev, C):
-    rng = np.random.default_rng(52)
     x = workloads.normal_rows(53, 300, C)
-    table = rng.integers(-1, 300, size=1001).astype(np.int32)
-    table[::7] = 300
-    table[::11] = -5
-    table[::13] = np.iinfo(np.int32).min
-    table[::17] = np.iinfo(np.int32).max
+    table = workloads.table_with_bad_entries(52, 1001, 300)
     tt = to_dev(table, dev)
     out = host(lwg.window_gather(to_dev(x, dev), tt))
     assert_bit_exact(out, oracle.window_gather(x, table), "gather with bad entries")

@@ -190,3 +190,37 @@ def id_tagged_rows(seed: int, rows: int, channels: int, block: int = 4096) -> np
     out[:, 2] = ids >> 20
     out[:, 3] = 1.0
     return out
+
+
+def gelu_inputs(seed: int, rows: int, cols: int):
+    """float32 ``x`` [rows, cols] and ``bias`` [cols], both i.i.d. N(0,1) drawn
+    in float64 and rounded to float32 (the bias + GELU operator takes float32)."""
+    rng = np.random.default_rng(seed)
+    x = rng.normal(0.0, 1.0, size=(rows, cols)).astype(np.float32)
+    bias = rng.normal(0.0, 1.0, size=cols).astype(np.float32)
+    return x, bias
+
+
+def fp16_bit_pattern_pairs(seed: int, rows: int, cols: int):
+    """(residual, branch) float16 [rows, cols] with every bit pattern possible:
+    uniformly random 16-bit words (so subnormals, infinities and NaNs occur),
+    and on even rows a branch within a few ulps of the negated residual, so that
+    sums cancel and land on subnormals and zeros."""
+    rng = np.random.default_rng(seed)
+    res = rng.integers(0, 1 << 16, size=(rows, cols), dtype=np.uint32).astype(np.uint16)
+    br = rng.integers(0, 1 << 16, size=(rows, cols), dtype=np.uint32).astype(np.uint16)
+    near = (res[::2].astype(np.int32) ^ 0x8000) + rng.integers(-3, 4, size=(len(res[::2]), cols))
+    br[::2] = near.astype(np.uint16)
+    return res.view(np.float16), br.view(np.float16)
+
+
+def table_with_bad_entries(seed: int, n_out: int, n_src: int) -> np.ndarray:
+    """int32 [n_out] gather table of random entries in [-1, n_src), with entries
+    outside [0, n_src) planted at fixed strides: n_src, -5, INT32_MIN, INT32_MAX."""
+    rng = np.random.default_rng(seed)
+    table = rng.integers(-1, n_src, size=n_out).astype(np.int32)
+    table[::7] = n_src
+    table[::11] = -5
+    table[::13] = np.iinfo(np.int32).min
+    table[::17] = np.iinfo(np.int32).max
+    return table
