@@ -142,3 +142,53 @@ def test_window_inverse_other_windows(dev, window):
     for shift in [(0, 0, 0), (1, 2, 3), (5, 40, 100)]:
         inv = host(lwg.window_inverse_build(grid, window, shift, device=dev))
         assert np.array_equal(inv, oracle.window_inverse_table(grid, window, shift)), (window, shift)
+
+
+def test_in_place_calls_at_level2_size(dev):
+    """In-place use at [32760, 384], where the capped, pipelined grids give each
+    wave more than one row tile (the next tile is read before the current one is
+    written). Every in-place result equals the out-of-place one bit for bit."""
+    lv = workloads.LEVEL2
+    n, c = lv.tokens, lv.channels
+    x = workloads.normal_rows(81, n, c, mean=0.2, std=1.5)
+    res = workloads.normal_rows(82, n, c, std=0.5)
+    gamma = workloads.normal_rows(83, 1, c)[0]
+    beta = workloads.normal_rows(84, 1, c, std=0.1)[0]
+    tg, tbeta = to_dev(gamma, dev), to_dev(beta, dev)
+
+    ref = host(lwg.ln_fixed(to_dev(x, dev)))
+    tx = to_dev(x, dev)
+    lwg.ln_fixed(tx, out=tx)
+    assert_bit_exact(host(tx), ref, "ln_fixed in place at level 2")
+
+    r_ref, y_ref = (host(t) for t in lwg.add_ln(to_dev(x, dev), to_dev(res, dev)))
+    assert_bit_exact(r_ref, oracle.residual_sum(res, x), "add_ln residual at level 2")
+    tb, tr = to_dev(x, dev), to_dev(res, dev)
+    lwg.add_ln(tb, tr, residual_out=tr, out=tb)
+    assert_bit_exact(host(tr), r_ref, "add_ln residual in place")
+    assert_bit_exact(host(tb), y_ref, "add_ln y over the branch")
+
+    r_ref, y_ref = (host(t) for t in lwg.add_ln_affine(to_dev(x, dev), to_dev(res, dev), tg, tbeta))
+    tb, tr = to_dev(x, dev), to_dev(res, dev)
+    lwg.add_ln_affine(tb, tr, tg, tbeta, residual_out=tr, out=tb)
+    assert_bit_exact(host(tr), r_ref, "add_ln_affine residual in place")
+    assert_bit_exact(host(tb), y_ref, "add_ln_affine y over the branch")
+
+    ref = host(lwg.ln_affine(to_dev(x, dev), tg, tbeta))
+    tx = to_dev(x, dev)
+    lwg.ln_affine(tx, tg, tbeta, out=tx)
+    assert_bit_exact(host(tx), ref, "ln_affine in place at level 2")
+
+    table = lwg.window_table(lv.grid, WINDOW, SHIFT, device=dev)
+    inv = lwg.window_inverse_table(lv.grid, WINDOW, SHIFT, device=dev)
+    win = workloads.normal_rows(85, table.numel(), c)
+    r_ref, y_ref = (host(t) for t in lwg.window_reverse_add_ln(to_dev(win, dev), inv, to_dev(res, dev)))
+    tr = to_dev(res, dev)
+    lwg.window_reverse_add_ln(to_dev(win, dev), inv, tr, residual_out=tr)
+    assert_bit_exact(host(tr), r_ref, "window_reverse_add_ln residual in place")
+
+    r_ref, g_ref = (host(t) for t in lwg.add_norm_gather(to_dev(x, dev), to_dev(res, dev), table))
+    tb, tr = to_dev(x, dev), to_dev(res, dev)
+    _, g = lwg.add_norm_gather(tb, tr, table, residual_out=tr)
+    assert_bit_exact(host(tr), r_ref, "add_norm_gather residual in place")
+    assert_bit_exact(host(g), g_ref, "add_norm_gather out with the residual in place")
