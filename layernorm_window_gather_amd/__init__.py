@@ -223,9 +223,17 @@ def window_index_build(grid, window, shift=(0, 0, 0), device=None, out: torch.Te
 _tables = {}
 
 
+def _settle(t: torch.Tensor) -> None:
+    """Wait for a newly built cached table, so that any stream may read it later.
+    Inside stream capture the build is part of the graph and no wait is made."""
+    if not torch.cuda.is_current_stream_capturing():
+        torch.cuda.current_stream(t.device).synchronize()
+
+
 def window_table(grid, window, shift=(0, 0, 0), device=None) -> torch.Tensor:
     """Cached ``window_index_build``: one table per (grid, window, shift, device).
-    The table is built on the device's current stream at first use."""
+    The table is built on the device's current stream at first use, and that
+    first call waits for it, so later calls may use it on any stream."""
     g, w, s = _triple(grid, "grid"), _triple(window, "window"), _triple(shift, "shift")
     dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
     if dev.index is None:
@@ -234,6 +242,7 @@ def window_table(grid, window, shift=(0, 0, 0), device=None) -> torch.Tensor:
     t = _tables.get(key)
     if t is None:
         t = window_index_build(g, w, s, device=dev)
+        _settle(t)
         _tables[key] = t
     return t
 
@@ -306,7 +315,8 @@ _inverses = {}
 
 
 def window_inverse_table(grid, window, shift=(0, 0, 0), device=None) -> torch.Tensor:
-    """Cached ``window_inverse_build``: one table per (grid, window, shift, device)."""
+    """Cached ``window_inverse_build``: one table per (grid, window, shift, device),
+    waited for at first use like ``window_table``."""
     g, w, s = _triple(grid, "grid"), _triple(window, "window"), _triple(shift, "shift")
     dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
     if dev.index is None:
@@ -315,6 +325,7 @@ def window_inverse_table(grid, window, shift=(0, 0, 0), device=None) -> torch.Te
     t = _inverses.get(key)
     if t is None:
         t = window_inverse_build(g, w, s, device=dev)
+        _settle(t)
         _inverses[key] = t
     return t
 

@@ -373,3 +373,18 @@ def test_runs_on_the_callers_stream(dev):
     s.synchronize()
     assert_ln_close(y.cpu().numpy(), oracle.layer_norm(x), "ln on side stream")
     assert_ln_close(y2.cpu().numpy(), oracle.layer_norm(oracle.layer_norm(x)), "chained on side stream")
+
+
+def test_cached_tables_built_on_one_stream_serve_another(dev):
+    """A cached table first built on a side stream is complete when the call
+    returns, and gathers on the default stream read it correctly."""
+    grid = (3, 11, 25)
+    x = workloads.normal_rows(95, int(np.prod(grid)), 192)
+    side = torch.cuda.Stream(device=dev)
+    with torch.cuda.stream(side):
+        t = lwg.window_table(grid, WINDOW, SHIFT, device=dev)
+        inv = lwg.window_inverse_table(grid, WINDOW, SHIFT, device=dev)
+    out = host(lwg.window_gather(to_dev(x, dev), t))
+    assert_bit_exact(out, oracle.window_gather(x, oracle.window_index_table(grid, WINDOW, SHIFT)),
+                     "gather with a table built on another stream")
+    assert np.array_equal(host(inv), oracle.window_inverse_table(grid, WINDOW, SHIFT))
