@@ -192,3 +192,38 @@ def test_in_place_calls_at_level2_size(dev):
     _, g = lwg.add_norm_gather(tb, tr, table, residual_out=tr)
     assert_bit_exact(host(tr), r_ref, "add_norm_gather residual in place")
     assert_bit_exact(host(g), g_ref, "add_norm_gather out with the residual in place")
+
+
+@pytest.mark.parametrize("C", [192, 384, 768])
+@pytest.mark.parametrize("eps", [1e-3, 0.5])
+def test_eps_reaches_every_layernorm_kernel(dev, C, eps):
+    """Every LayerNorm-family call honours its eps. Rows have variance 2.5e-3, so
+    eps = 1e-3 or 0.5 moves every output far outside the tolerance of the
+    default 1e-5."""
+    grid = (2, 7, 13)
+    n = int(np.prod(grid))
+    x = workloads.normal_rows(91, n, C, mean=0.1, std=0.05)
+    res = workloads.normal_rows(92, n, C, std=0.05)
+    gamma = workloads.normal_rows(93, 1, C)[0]
+    beta = workloads.normal_rows(94, 1, C, std=0.1)[0]
+    table = oracle.window_index_table(grid, WINDOW, SHIFT)
+    win = workloads.normal_rows(96, table.size, C, std=0.05)
+    tx, tr, tg, tb = to_dev(x, dev), to_dev(res, dev), to_dev(gamma, dev), to_dev(beta, dev)
+    tt = lwg.window_index_build(grid, WINDOW, SHIFT, device=dev)
+    inv = lwg.window_inverse_build(grid, WINDOW, SHIFT, device=dev)
+    tag = f"C={C} eps={eps}"
+    assert_ln_close(host(lwg.ln_fixed(tx, eps=eps)), oracle.layer_norm(x, eps), f"ln_fixed {tag}")
+    _, y = lwg.add_ln(tx, tr, eps=eps)
+    assert_ln_close(host(y), oracle.add_ln(x, res, eps)[1], f"add_ln {tag}")
+    assert_ln_close(host(lwg.norm_gather(tx, tt, eps=eps)), oracle.norm_gather(x, table, eps), f"norm_gather {tag}")
+    _, g = lwg.add_norm_gather(tx, tr, tt, eps=eps)
+    assert_ln_close(host(g), oracle.add_norm_gather(x, res, table, eps)[1], f"add_norm_gather {tag}")
+    _, y = lwg.window_reverse_add_ln(to_dev(win, dev), inv, tr, eps=eps)
+    assert_ln_close(host(y), oracle.window_reverse_add_ln(win, res, grid, WINDOW, SHIFT, eps)[1],
+                    f"window_reverse_add_ln {tag}")
+    assert_ln_close(host(lwg.ln_affine(tx, tg, tb, eps=eps)), oracle.layer_norm_affine(x, gamma, beta, eps),
+                    f"ln_affine {tag}")
+    _, y = lwg.add_ln_affine(tx, tr, tg, tb, eps=eps)
+    assert_ln_close(host(y), oracle.add_ln_affine(x, res, gamma, beta, eps)[1], f"add_ln_affine {tag}")
+    # the default eps would give visibly different rows
+    assert np.abs(oracle.layer_norm(x, eps).astype(np.float64) - oracle.layer_norm(x).astype(np.float64)).max() > 0.1
