@@ -109,3 +109,21 @@ def test_affine_parameter_checks(dev):
         lwg.ln_affine(x, torch.ones(191, dtype=torch.float16, device=dev), torch.zeros(192, dtype=torch.float16, device=dev))
     with pytest.raises(RuntimeError, match="beta"):
         lwg.ln_affine(x, torch.ones(192, dtype=torch.float16, device=dev), torch.zeros(192, dtype=torch.float32, device=dev))
+
+
+@pytest.mark.parametrize("level,seed", [(workloads.LEVEL1, 31), (workloads.LEVEL2, 32)])
+def test_affine_full_size(dev, level, seed):
+    """Both affine kernels at the workload sizes, where the C = 384 grids are
+    capped and waves take several row tiles."""
+    n, c = level.tokens, level.channels
+    nc, off = workloads.stress_row_classes(seed, n)
+    res = workloads.mixed_rows(seed + 1, n, c, nc, off)
+    br = workloads.mixed_rows(seed + 2, n, c, nc, off, offset_mean=0.0)
+    g, b = _params(c, seed + 3)
+    tg, tb_ = to_dev(g, dev), to_dev(b, dev)
+    y = host(lwg.ln_affine(to_dev(res, dev), tg, tb_))
+    assert_ln_close(y, oracle.layer_norm_affine(res, g, b), f"ln_affine {level.name}")
+    r, y = lwg.add_ln_affine(to_dev(br, dev), to_dev(res, dev), tg, tb_)
+    r_ref, y_ref = oracle.add_ln_affine(br, res, g, b)
+    assert_bit_exact(host(r), r_ref, f"add_ln_affine residual {level.name}")
+    assert_ln_close(host(y), y_ref, f"add_ln_affine {level.name}")
