@@ -388,3 +388,17 @@ def test_cached_tables_built_on_one_stream_serve_another(dev):
     assert_bit_exact(out, oracle.window_gather(x, oracle.window_index_table(grid, WINDOW, SHIFT)),
                      "gather with a table built on another stream")
     assert np.array_equal(host(inv), oracle.window_inverse_table(grid, WINDOW, SHIFT))
+
+
+@pytest.mark.parametrize("shift", [SHIFT, NO_SHIFT])
+def test_level2_norm_gather_and_gather_full(dev, shift):
+    """norm_gather and window_gather on the whole level-2 tensor [32760, 384]
+    (capped, pipelined grid: waves take 1.5 tiles), every row compared."""
+    x, _, scaled = workloads.level2_inputs()
+    table = oracle.window_index_table(LEVEL2.grid, WINDOW, shift)
+    tt = lwg.window_index_build(LEVEL2.grid, WINDOW, shift, device=dev)
+    tx = to_dev(x, dev)
+    ng = host(lwg.norm_gather(tx, tt))
+    assert_ln_close(ng, oracle.norm_gather(x, table), f"level2 norm_gather shift={shift}")
+    assert not bits(ng[table < 0]).any()
+    assert_bit_exact(host(lwg.window_gather(tx, tt)), oracle.window_gather(x, table), f"level2 gather shift={shift}")
