@@ -288,6 +288,59 @@ def next_ops_gate(lwg, torch, dev, host, levels):
     return True
 
 
+SWEEP_ROWS = (16384, 32768, 65536, 131040, 262144, 524288)
+
+
+def size_sweep(lwg, torch, dev, reps):
+    """add_ln and ln_fixed at C = 192 over SWEEP_ROWS, each on a cold buffer pool,
+    timed like the per-kernel table; a least-squares fit of time = fixed + bytes /
+    rate separates the per-launch fixed cost from the streaming rate."""
+    c = 192
+    base = workloads.normal_rows(9, 1 << 16, c)
+    out = {"C": c, "rows": list(SWEEP_ROWS), "add_ln_us": [], "ln_fixed_us": []}
+
+    def timed(pool):
+        for f in pool:
+            f()
+        torch.cuda.synchronize()
+        runs = []
+        for _ in range(5):
+            torch.cuda._sleep(SPIN_CYCLES)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for i in range(reps):
+                pool[i % len(pool)]()
+            b.record()
+            b.synchronize()
+            runs.append(a.elapsed_time(b) * 1e3 / reps)
+        return float(np.median(runs))
+
+    for rows in SWEEP_ROWS:
+        x0 = torch.from_numpy(np.resize(base, (rows, c))).to(dev)
+        for op, nbytes in (("add_ln", 4 * rows * c * HALF), ("ln_fixed", 2 * rows * c * HALF)):
+            count = max(3, -(-COLD_BYTES // nbytes) + 1)
+            pool = []
+            for _ in range(count):
+                if op == "add_ln":
+                    b, r = x0.clone(), x0.clone()
+                    pool.append(lwg.prepare(op, b, r, torch.empty_like(r), torch.empty_like(r)))
+                else:
+                    xx = x0.clone()
+                    pool.append(lwg.prepare(op, xx, torch.empty_like(xx)))
+            out[f"{op}_us"].append(round(timed(pool), 3))
+            del pool
+            torch.cuda.empty_cache()
+    fit = {}
+    for op, per_row in (("add_ln", 4 * c * HALF), ("ln_fixed", 2 * c * HALF)):
+        nb = np.array([r * per_row for r in SWEEP_ROWS], dtype=np.float64)
+        us = np.array(out[f"{op}_us"])
+        (fixed, slope), *_ = np.linalg.lstsq(np.vstack([np.ones_like(nb), nb]).T, us, rcond=None)
+        fit[op] = {"fixed_us": round(float(fixed), 2), "marginal_GBps": round(1e-3 / float(slope), 1),
+                   "pct_of_peak_at_sizes": [round(100 * b / (t * 1e3) / PEAK_GBS, 1) for b, t in zip(nb, us)]}
+    out["fit"] = fit
+    return out
+
+
 def memory_attributes(dev_index: int):
     """The device's reported memory clock (kHz) and bus width (bits), read with
     hipDeviceGetAttribute, and the figure clock x bus width x 2 transfers per
@@ -388,6 +441,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=OPS + NEXT_OPS + ("all",), default=None,
                     help="launch only this op (or every op), --steps times per level (profiling runs)")
+    ap.add_argument("--size-sweep", action="store_true",
+                    help="time add_ln and ln_fixed at C=192 over a range of row counts and fit fixed cost + rate")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="also run an elementwise copy of this many MiB (PMC calibration)")
     args = ap.parse_args(argv)
@@ -424,6 +479,9 @@ def main(argv=None):
     torch.cuda.synchronize()
 
     parity_gate(lwg, torch, sets, host, levels, m_of)
+    if args.size_sweep:
+        print(json.dumps({"size_sweep": size_sweep(lwg, torch, dev, args.kernel_reps)}), flush=True)
+        return 0
     if args.only is None:
         next_ops_gate(lwg, torch, dev, host, levels)
 
