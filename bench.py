@@ -297,7 +297,7 @@ def size_sweep(lwg, torch, dev, reps):
     rate separates the per-launch fixed cost from the streaming rate."""
     c = 192
     base = workloads.normal_rows(9, 1 << 16, c)
-    out = {"C": c, "rows": list(SWEEP_ROWS), "add_ln_us": [], "ln_fixed_us": []}
+    out = {"C": c, "rows": list(SWEEP_ROWS), "add_ln_us": [], "ln_fixed_us": [], "torch_copy_us": []}
 
     def timed(pool):
         for f in pool:
@@ -317,21 +317,25 @@ def size_sweep(lwg, torch, dev, reps):
 
     for rows in SWEEP_ROWS:
         x0 = torch.from_numpy(np.resize(base, (rows, c))).to(dev)
-        for op, nbytes in (("add_ln", 4 * rows * c * HALF), ("ln_fixed", 2 * rows * c * HALF)):
+        for op, nbytes in (("add_ln", 4 * rows * c * HALF), ("ln_fixed", 2 * rows * c * HALF),
+                           ("torch_copy", 2 * rows * c * HALF)):
             count = max(3, -(-COLD_BYTES // nbytes) + 1)
             pool = []
             for _ in range(count):
                 if op == "add_ln":
                     b, r = x0.clone(), x0.clone()
                     pool.append(lwg.prepare(op, b, r, torch.empty_like(r), torch.empty_like(r)))
-                else:
+                elif op == "ln_fixed":
                     xx = x0.clone()
                     pool.append(lwg.prepare(op, xx, torch.empty_like(xx)))
+                else:   # the platform's own device copy, for reference
+                    src, dst = x0.clone(), torch.empty_like(x0)
+                    pool.append(lambda src=src, dst=dst: dst.copy_(src))
             out[f"{op}_us"].append(round(timed(pool), 3))
             del pool
             torch.cuda.empty_cache()
     fit = {}
-    for op, per_row in (("add_ln", 4 * c * HALF), ("ln_fixed", 2 * c * HALF)):
+    for op, per_row in (("add_ln", 4 * c * HALF), ("ln_fixed", 2 * c * HALF), ("torch_copy", 2 * c * HALF)):
         nb = np.array([r * per_row for r in SWEEP_ROWS], dtype=np.float64)
         us = np.array(out[f"{op}_us"])
         (fixed, slope), *_ = np.linalg.lstsq(np.vstack([np.ones_like(nb), nb]).T, us, rcond=None)
