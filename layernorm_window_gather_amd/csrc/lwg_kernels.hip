@@ -265,18 +265,23 @@ __device__ __forceinline__ int64_t wave_stride() {
     return static_cast<int64_t>(gridDim.x) * (kBlock / 64);
 }
 
-// The K chunks this lane holds of row tile w (zeros past the last row).
-template <int C, int K, class H>
+// The K chunks this lane holds of row tile w (zeros past the last row). With
+// kPrio > 0 the wave issues the loads at that scheduling priority (s_setprio)
+// and drops back to 0 after them, so that a wave with loads to issue goes ahead
+// of waves busy with row arithmetic on the same SIMD.
+template <int C, int K, class H, int kPrio = 0>
 __device__ __forceinline__ void load_tile(const chunk_t* x, int64_t w, int64_t rows, int lane,
                                           chunk_t (&v)[K]) {
     using T = Tile<C, K>;
     const int64_t row = w * T::kRowsPerWave + lane / T::kLanes;
     zero(v);
+    if constexpr (kPrio > 0) __builtin_amdgcn_s_setprio(kPrio);
     if (row < rows) {
         const int64_t base = row * T::kChunks + lane % T::kLanes;
 #pragma unroll
         for (int k = 0; k < K; ++k) v[k] = load16<H>(x + base + k * T::kLanes);
     }
+    if constexpr (kPrio > 0) __builtin_amdgcn_s_setprio(0);
 }
 
 template <int C, int K, class H>
@@ -339,7 +344,7 @@ __global__ __launch_bounds__(kBlock) void ln_fixed_kernel(const chunk_t* x, chun
 
 // residual_out and y may alias the inputs: each lane reads its chunks of a row
 // before it writes any, and the prefetched tile is a different set of rows.
-template <int C, int K, class H, bool kPrefetch>
+template <int C, int K, class H, bool kPrefetch, int kPrio>
 __global__ __launch_bounds__(kBlock) void add_ln_kernel(const chunk_t* branch, const chunk_t* residual,
                                                         chunk_t* residual_out, chunk_t* y,
                                                         int64_t rows, double eps) {
@@ -348,13 +353,13 @@ __global__ __launch_bounds__(kBlock) void add_ln_kernel(const chunk_t* branch, c
     const int64_t stride = wave_stride();
     int64_t w = first_wave();
     chunk_t b[K], r[K];
-    load_tile<C, K, H>(branch, w, rows, lane, b);
-    load_tile<C, K, H>(residual, w, rows, lane, r);
+    load_tile<C, K, H, kPrio>(branch, w, rows, lane, b);
+    load_tile<C, K, H, kPrio>(residual, w, rows, lane, r);
     for (; w * T::kRowsPerWave < rows; w += stride) {
         chunk_t nb[K], nr[K];
         if constexpr (kPrefetch) {
-            load_tile<C, K, H>(branch, w + stride, rows, lane, nb);
-            load_tile<C, K, H>(residual, w + stride, rows, lane, nr);
+            load_tile<C, K, H, kPrio>(branch, w + stride, rows, lane, nb);
+            load_tile<C, K, H, kPrio>(residual, w + stride, rows, lane, nr);
         }
         residual_add<K>(b, r);
         store_tile<C, K, H>(residual_out, w, rows, lane, r);
@@ -367,8 +372,8 @@ __global__ __launch_bounds__(kBlock) void add_ln_kernel(const chunk_t* branch, c
                 r[k] = nr[k];
             }
         } else {
-            load_tile<C, K, H>(branch, w + stride, rows, lane, b);
-            load_tile<C, K, H>(residual, w + stride, rows, lane, r);
+            load_tile<C, K, H, kPrio>(branch, w + stride, rows, lane, b);
+            load_tile<C, K, H, kPrio>(residual, w + stride, rows, lane, r);
         }
     }
 }
@@ -387,7 +392,7 @@ __device__ __forceinline__ void stage_params(chunk_t* params, const chunk_t* gam
     __syncthreads();
 }
 
-template <int C, int K, class H>
+template <int C, int K, class H, int kPrio>
 __global__ __launch_bounds__(kBlock) void ln_affine_kernel(const chunk_t* x, const chunk_t* gamma,
                                                            const chunk_t* beta, chunk_t* y,
                                                            int64_t rows, double eps) {
@@ -401,18 +406,18 @@ __global__ __launch_bounds__(kBlock) void ln_affine_kernel(const chunk_t* x, con
     const int64_t stride = wave_stride();
     int64_t w = first_wave();
     chunk_t v[K];
-    load_tile<C, K, H>(x, w, rows, lane, v);
+    load_tile<C, K, H, kPrio>(x, w, rows, lane, v);
     for (; w * T::kRowsPerWave < rows; w += stride) {
         // re-read gamma/beta from LDS per row tile instead of letting the
         // compiler hoist 2*K widened chunks out of the loop into registers
         asm volatile("" ::: "memory");
         layer_norm_affine_lane<C, K>(v, gamma, beta, sub, eps);
         store_tile<C, K, H>(y, w, rows, lane, v);
-        load_tile<C, K, H>(x, w + stride, rows, lane, v);
+        load_tile<C, K, H, kPrio>(x, w + stride, rows, lane, v);
     }
 }
 
-template <int C, int K, class H, bool kPrefetch>
+template <int C, int K, class H, bool kPrefetch, int kPrio>
 __global__ __launch_bounds__(kBlock) void add_ln_affine_kernel(const chunk_t* branch, const chunk_t* residual,
                                                                  const chunk_t* gamma, const chunk_t* beta,
                                                                  chunk_t* residual_out, chunk_t* y,
@@ -427,13 +432,13 @@ __global__ __launch_bounds__(kBlock) void add_ln_affine_kernel(const chunk_t* br
     const int64_t stride = wave_stride();
     int64_t w = first_wave();
     chunk_t b[K], r[K];
-    load_tile<C, K, H>(branch, w, rows, lane, b);
-    load_tile<C, K, H>(residual, w, rows, lane, r);
+    load_tile<C, K, H, kPrio>(branch, w, rows, lane, b);
+    load_tile<C, K, H, kPrio>(residual, w, rows, lane, r);
     for (; w * T::kRowsPerWave < rows; w += stride) {
         chunk_t nb[K], nr[K];
         if constexpr (kPrefetch) {
-            load_tile<C, K, H>(branch, w + stride, rows, lane, nb);
-            load_tile<C, K, H>(residual, w + stride, rows, lane, nr);
+            load_tile<C, K, H, kPrio>(branch, w + stride, rows, lane, nb);
+            load_tile<C, K, H, kPrio>(residual, w + stride, rows, lane, nr);
         }
         asm volatile("" ::: "memory");  // as in ln_affine_kernel: no hoisting of gamma/beta
         residual_add<K>(b, r);
@@ -447,8 +452,8 @@ __global__ __launch_bounds__(kBlock) void add_ln_affine_kernel(const chunk_t* br
                 r[k] = nr[k];
             }
         } else {
-            load_tile<C, K, H>(branch, w + stride, rows, lane, b);
-            load_tile<C, K, H>(residual, w + stride, rows, lane, r);
+            load_tile<C, K, H, kPrio>(branch, w + stride, rows, lane, b);
+            load_tile<C, K, H, kPrio>(residual, w + stride, rows, lane, r);
         }
     }
 }
@@ -520,7 +525,7 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(const chunk_t* __restric
 // a zero branch. residual_out and y may alias residual (row i is read and
 // written by the same lanes; a prefetched tile holds other rows); neither may
 // overlap win, whose rows a prefetch may read after another row was written.
-template <int C, int K, class H, bool kPrefetch>
+template <int C, int K, class H, bool kPrefetch, int kPrio>
 __global__ __launch_bounds__(kBlock) void reverse_add_ln_kernel(
     const chunk_t* __restrict__ win, int64_t n_win, const int32_t* __restrict__ idx,
     const chunk_t* residual, chunk_t* residual_out, chunk_t* y, int64_t rows, double eps) {
@@ -530,12 +535,12 @@ __global__ __launch_bounds__(kBlock) void reverse_add_ln_kernel(
     int64_t w = first_wave();
     chunk_t b[K], r[K];
     load_gathered<C, K, H>(win, n_win, idx, rows, w, lane, b);
-    load_tile<C, K, H>(residual, w, rows, lane, r);
+    load_tile<C, K, H, kPrio>(residual, w, rows, lane, r);
     for (; w * T::kRowsPerWave < rows; w += stride) {
         chunk_t nb[K], nr[K];
         if constexpr (kPrefetch) {
             load_gathered<C, K, H>(win, n_win, idx, rows, w + stride, lane, nb);
-            load_tile<C, K, H>(residual, w + stride, rows, lane, nr);
+            load_tile<C, K, H, kPrio>(residual, w + stride, rows, lane, nr);
         }
         residual_add<K>(b, r);
         store_tile<C, K, H>(residual_out, w, rows, lane, r);
@@ -549,7 +554,7 @@ __global__ __launch_bounds__(kBlock) void reverse_add_ln_kernel(
             }
         } else {
             load_gathered<C, K, H>(win, n_win, idx, rows, w + stride, lane, b);
-            load_tile<C, K, H>(residual, w + stride, rows, lane, r);
+            load_tile<C, K, H, kPrio>(residual, w + stride, rows, lane, r);
         }
     }
 }
@@ -755,16 +760,23 @@ using Streaming = Hints<true, true>;
 //  * C = 192, one tile per wave: the pipelined form of ln_fixed, add_ln and the
 //    fused residual kernels issues the tile's loads ahead of the loop test and
 //    measured 2-4% faster; the gathers and ln_affine are fastest as they are.
+//  * kPriority: the pipelined two-input kernels at C = 384 and ln_affine at
+//    C = 192 issue their loads at wave priority 1 (s_setprio) and drop to 0
+//    for the arithmetic: C = 384 add_ln -7%, add_ln_affine -5%,
+//    window_reverse_add_ln -1%, C = 192 ln_affine -2.5%. On the one-tile-per-
+//    wave kernels it cost up to 4% and is off.
 //  * C = 768 and everything else: the default.
 template <int C, Op O> struct Launch {
     using H = Streaming;
     static constexpr int kBlocksPerCu = 0;
     static constexpr bool kPrefetch = false;
+    static constexpr int kPriority = 0;
 };
-template <int Cap, bool Prefetch> struct Tuned {
+template <int Cap, bool Prefetch, int Priority = 0> struct Tuned {
     using H = Streaming;
     static constexpr int kBlocksPerCu = Cap;
     static constexpr bool kPrefetch = Prefetch;
+    static constexpr int kPriority = Priority;
 };
 template <> struct Launch<192, Op::kLn> : Tuned<0, true> {};
 template <> struct Launch<192, Op::kAddLn> : Tuned<0, true> {};
@@ -773,10 +785,11 @@ template <> struct Launch<192, Op::kAddNormGather> : Tuned<0, true> {};
 template <> struct Launch<192, Op::kAddLnAffine> : Tuned<0, true> {};
 template <> struct Launch<384, Op::kLn> : Tuned<3, true> {};
 template <> struct Launch<384, Op::kNormGather> : Tuned<3, true> {};
-template <> struct Launch<384, Op::kAddLn> : Tuned<2, true> {};
-template <> struct Launch<384, Op::kReverseAddLn> : Tuned<2, true> {};
-template <> struct Launch<384, Op::kAddLnAffine> : Tuned<2, true> {};
+template <> struct Launch<384, Op::kAddLn> : Tuned<2, true, 1> {};
+template <> struct Launch<384, Op::kReverseAddLn> : Tuned<2, true, 1> {};
+template <> struct Launch<384, Op::kAddLnAffine> : Tuned<2, true, 1> {};
 template <> struct Launch<384, Op::kLnAffine> : Tuned<3, false> {};
+template <> struct Launch<192, Op::kLnAffine> : Tuned<0, false, 1> {};
 template <> struct Launch<384, Op::kAddNormGather> : Tuned<2, false> {};
 
 
@@ -823,7 +836,7 @@ template <int C>
 hipError_t add_ln_c(const void* b, const void* r, void* ro, void* y, int64_t rows, double eps,
                     hipStream_t s) {
     using L = Launch<C, Op::kAddLn>;
-    add_ln_kernel<C, Width<C>::K, typename L::H, L::kPrefetch><<<grid_for<C, Op::kAddLn>(rows), kBlock, 0, s>>>(
+    add_ln_kernel<C, Width<C>::K, typename L::H, L::kPrefetch, L::kPriority><<<grid_for<C, Op::kAddLn>(rows), kBlock, 0, s>>>(
         static_cast<const chunk_t*>(b), static_cast<const chunk_t*>(r), static_cast<chunk_t*>(ro),
         static_cast<chunk_t*>(y), rows, eps);
     return hipGetLastError();
@@ -889,7 +902,7 @@ template <int C>
 hipError_t reverse_add_ln_c(const void* win, int64_t n_win, const int32_t* idx, const void* r, void* ro,
                             void* y, int64_t rows, double eps, hipStream_t s) {
     using L = Launch<C, Op::kReverseAddLn>;
-    reverse_add_ln_kernel<C, Width<C>::K, typename L::H, L::kPrefetch>
+    reverse_add_ln_kernel<C, Width<C>::K, typename L::H, L::kPrefetch, L::kPriority>
         <<<grid_for<C, Op::kReverseAddLn>(rows), kBlock, 0, s>>>(
             static_cast<const chunk_t*>(win), n_win, idx, static_cast<const chunk_t*>(r),
             static_cast<chunk_t*>(ro), static_cast<chunk_t*>(y), rows, eps);
@@ -923,7 +936,7 @@ template <int C>
 hipError_t ln_affine_c(const void* x, const void* g, const void* b, void* y, int64_t rows, double eps,
                        hipStream_t s) {
     using L = Launch<C, Op::kLnAffine>;
-    ln_affine_kernel<C, Width<C>::K, typename L::H><<<grid_for<C, Op::kLnAffine>(rows), kBlock, 0, s>>>(
+    ln_affine_kernel<C, Width<C>::K, typename L::H, L::kPriority><<<grid_for<C, Op::kLnAffine>(rows), kBlock, 0, s>>>(
         static_cast<const chunk_t*>(x), static_cast<const chunk_t*>(g), static_cast<const chunk_t*>(b),
         static_cast<chunk_t*>(y), rows, eps);
     return hipGetLastError();
@@ -938,7 +951,7 @@ template <int C>
 hipError_t add_ln_affine_c(const void* br, const void* r, const void* g, const void* b, void* ro, void* y,
                            int64_t rows, double eps, hipStream_t s) {
     using L = Launch<C, Op::kAddLnAffine>;
-    add_ln_affine_kernel<C, Width<C>::K, typename L::H, L::kPrefetch>
+    add_ln_affine_kernel<C, Width<C>::K, typename L::H, L::kPrefetch, L::kPriority>
         <<<grid_for<C, Op::kAddLnAffine>(rows), kBlock, 0, s>>>(
             static_cast<const chunk_t*>(br), static_cast<const chunk_t*>(r), static_cast<const chunk_t*>(g),
             static_cast<const chunk_t*>(b), static_cast<chunk_t*>(ro), static_cast<chunk_t*>(y), rows, eps);
