@@ -38,3 +38,23 @@ def test_abi_checks_under_asan_and_ubsan(tmp_path):
     run = subprocess.run([str(exe), "200000"], capture_output=True, text=True, timeout=300, env=env)
     assert run.returncode == 0, run.stdout + run.stderr
     assert "0 launcher precondition violations, 0 failures" in run.stdout, run.stdout
+
+
+def test_multiply_shift_division_is_exact(tmp_path):
+    """make_fastdiv (the reciprocals the window-table kernels divide by): exact
+    for every divisor up to 2^16 and sampled divisors up to 2^31 - 1, at the
+    dividends around the first and last multiples below 2^31 and at random
+    points (tests/sanitize/fastdiv_check.cpp)."""
+    gxx = shutil.which("g++")
+    if gxx is None or not os.path.exists(os.path.join(ROCM, "include", "hip", "hip_runtime.h")):
+        pytest.skip("g++ or the HIP headers are not available")
+    exe = tmp_path / "fastdiv_check"
+    cmd = [gxx, "-std=c++17", "-O2", "-fsanitize=undefined", "-fno-sanitize-recover=all",
+           "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROCM, "include"),
+           "-I", os.path.join(ROOT, "layernorm_window_gather_amd", "csrc"),
+           os.path.join(HERE, "fastdiv_check.cpp"), "-o", str(exe)]
+    build = subprocess.run(cmd, capture_output=True, text=True, timeout=300)
+    assert build.returncode == 0, build.stderr
+    run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=300)
+    assert run.returncode == 0, run.stdout + run.stderr
+    assert " 0 wrong" in run.stdout, run.stdout
