@@ -127,3 +127,47 @@ def test_affine_full_size(dev, level, seed):
     r_ref, y_ref = oracle.add_ln_affine(br, res, g, b)
     assert_bit_exact(host(r), r_ref, f"add_ln_affine residual {level.name}")
     assert_ln_close(host(y), y_ref, f"add_ln_affine {level.name}")
+
+
+@pytest.mark.parametrize("C", [192, 384, 768])
+def test_every_layernorm_rounds_once_next_to_a_midpoint(dev, C):
+    """A +-1 row has mean 0 and variance 1, so y = +-1/sqrt(1 + eps). With eps
+    chosen so that y lies 2**-30 below the binary16 midpoint 1 - 2**-12, a single
+    rounding gives 0x3BFF, while narrowing to binary32 first lands on the
+    midpoint and gives 0x3C00 by ties-to-even. Every kernel that normalises a
+    row must return 0x3BFF / 0xBBFF there, bit for bit with the oracle, at every
+    width (144 rows: one window of the (2, 6, 12) shape, so the reverse uses an
+    identity inverse table)."""
+    from decimal import Decimal, getcontext
+    getcontext().prec = 60
+    target = Decimal(1) - Decimal(2) ** -12 - Decimal(2) ** -30
+    eps = float(1 / (target * target) - 1)
+    n, half = 144, C // 2
+    x = workloads.normal_rows(700 + C, n, C, mean=0.1, std=1.3)
+    pm = np.array([1.0] * half + [-1.0] * half, dtype=np.float16)
+    crafted = [0, 1, 2, 77, n - 1]
+    x[0], x[1], x[2], x[77], x[n - 1] = pm, -pm, np.roll(pm, 5), pm[::-1], pm
+    ref = oracle.layer_norm(x, eps)
+    assert np.all(np.isin(bits(ref[crafted]), (0x3BFF, 0xBBFF)))
+    ones = np.ones(C, np.float16)
+    zeros = np.zeros(C, np.float16)
+    assert np.array_equal(bits(oracle.layer_norm_affine(x, ones, zeros, eps)), bits(ref))
+
+    xd, zd = to_dev(x, dev), torch.zeros(n, C, dtype=torch.float16, device=dev)
+    g1, b0 = to_dev(ones, dev), to_dev(zeros, dev)
+    ident = torch.arange(n, dtype=torch.int32, device=dev)
+    inv = lwg.window_inverse_table((2, 6, 12), WINDOW, NO_SHIFT, device=dev)
+    assert np.array_equal(host(inv), np.arange(n, dtype=np.int32))
+    outs = {
+        "ln_fixed": lwg.ln_fixed(xd, eps),
+        "add_ln": lwg.add_ln(xd, zd, eps)[1],
+        "norm_gather": lwg.norm_gather(xd, ident, eps),
+        "add_norm_gather": lwg.add_norm_gather(xd, zd, ident, eps)[1],
+        "window_reverse_add_ln": lwg.window_reverse_add_ln(xd, inv, zd, eps)[1],
+        "ln_affine": lwg.ln_affine(xd, g1, b0, eps),
+        "add_ln_affine": lwg.add_ln_affine(xd, zd, g1, b0, eps)[1],
+    }
+    for name, y in outs.items():
+        got = host(y)
+        assert_bit_exact(got[crafted], ref[crafted], f"{name} C={C} next to the midpoint")
+        assert_ln_close(got, ref, f"{name} C={C}")

@@ -8,7 +8,9 @@ the two binary16 residual operands in binary32 before the binary16 rounding.
 It must *pass*, because when such a sum is inexact in binary32 the smaller
 operand is below an eighth of a binary16 ulp of the larger, so both routes
 round to the same binary16 value (the reading of the FP16 residual in the
-design notes).
+design notes). A second equivalent edit normalises after the gather instead of
+before: a padding row is all +0.0, and the LayerNorm of a zero row is
+0 / sqrt(0 + eps) = +0.0, so the two orders agree.
 """
 import os
 import shutil
@@ -46,10 +48,32 @@ MISTAKES = {
                               "g = g.transpose(0, 3, 2, 4, 1, 5, 6)"),
     "add_norm_gather normalises the old residual": ("oracle/window.py", "    return r, norm_gather(r, table, eps)",
                                                     "    return r, norm_gather(residual, table, eps)"),
+    "binary16 rounding through binary32": ("oracle/rowops.py",
+                                           "return np.asarray(values, dtype=np.float64).astype(np.float16)",
+                                           "return np.asarray(values, dtype=np.float64).astype(np.float32)"
+                                           ".astype(np.float16)"),
+    "mean over the wrong axis": ("oracle/rowops.py", "mean = v.mean(axis=1, keepdims=True)",
+                                 "mean = v.mean(axis=0, keepdims=True)"),
+    "deviations not centred": ("oracle/rowops.py", "dev = v - mean", "dev = v"),
+    "padding as token 0": ("oracle/window.py", "constant_values=-1", "constant_values=0"),
+    "shift before padding": ("oracle/window.py",
+                             "    padded = np.pad(ids, pad, mode=\"constant\", constant_values=-1)\n"
+                             "    rolled = np.roll(padded, shift=tuple(-s for s in shift), axis=(0, 1, 2))",
+                             "    ids = np.roll(ids, shift=tuple(-s for s in shift), axis=(0, 1, 2))\n"
+                             "    padded = np.pad(ids, pad, mode=\"constant\", constant_values=-1)\n"
+                             "    rolled = padded"),
+    "tokens with w slowest": ("oracle/window.py", "ids = np.arange(Z * H * W, dtype=np.int64).reshape(Z, H, W)",
+                              "ids = np.arange(Z * H * W, dtype=np.int64).reshape(W, H, Z).transpose(2, 1, 0)"),
+    "reverse: crop at the low end": ("oracle/window.py", "g[:Z, :H, :W]", "g[Zp - Z:, Hp - H:, Wp - W:]"),
+    "gelu: sqrt(2/pi) dropped": ("oracle/activation.py", "np.tanh(GELU_K0 * (t + GELU_K1 * t ** 3))",
+                                 "np.tanh(t + GELU_K1 * t ** 3)"),
 }
 EQUIVALENT = {
     "residual added in binary32": ("oracle/rowops.py", "return fp16_round(r + b)",
                                    "return fp16_round(np.float32(r) + np.float32(b))"),
+    "norm_gather normalises after the gather": ("oracle/window.py",
+                                                "return window_gather(layer_norm(x, eps), table)",
+                                                "return layer_norm(window_gather(x, table), eps)"),
 }
 
 

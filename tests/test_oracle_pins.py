@@ -122,6 +122,24 @@ def test_ln_plus_minus_one_row(C):
 
 
 @pytest.mark.parametrize("C", [192, 384])
+def test_ln_rounds_once_from_binary64(C):
+    # A +-1 row has mean 0 and variance 1, so y = +-1/sqrt(1 + eps). eps is
+    # chosen so that y lies 2**-30 below the binary16 midpoint 1 - 2**-12.
+    # Rounded once, y goes down to 1 - 2**-11 (0x3BFF). Rounded to binary32
+    # first, it lands on the midpoint (binary32 spacing below 1 is 2**-24),
+    # and the tie then goes to even, 1.0 (0x3C00).
+    getcontext().prec = 60
+    target = Decimal(1) - Decimal(2) ** -12 - Decimal(2) ** -30
+    eps = float(1 / (target * target) - 1)
+    y_exact = 1 / (1 + Decimal(eps)).sqrt()
+    mid = Decimal(1) - Decimal(2) ** -12
+    assert Decimal(1) - Decimal(2) ** -11 < y_exact < mid and mid - y_exact > Decimal(2) ** -31
+    row = np.array([1.0] * (C // 2) + [-1.0] * (C // 2), dtype=np.float16)[None, :]
+    y = bits_of(oracle.layer_norm(row, eps))
+    assert np.all(y[0, : C // 2] == 0x3BFF) and np.all(y[0, C // 2:] == 0xBBFF), hex(int(y[0, 0]))
+
+
+@pytest.mark.parametrize("C", [192, 384])
 @pytest.mark.parametrize("value", [0.0, 3.5, -100.0, 65504.0])
 def test_ln_constant_row_is_plus_zero(C, value):
     row = np.full((1, C), value, dtype=np.float16)
