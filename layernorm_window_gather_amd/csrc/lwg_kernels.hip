@@ -734,7 +734,8 @@ __global__ __launch_bounds__(kBlock) void bias_gelu_kernel(const f32x4_t* x, con
 // and store-only-hinted accesses for every kernel. The grid is one tile per
 // wave unless the table of Launch entries below says otherwise. (K = 3 at
 // C = 384, 16 lanes per row, measured -2% on the gathers and +5% / +16% on
-// ln_fixed / ln_affine: not taken.)
+// ln_fixed / ln_affine; the normalising kernels keep K = 6 so that all of them
+// reduce a row alike, and only the plain gather takes K = 3.)
 enum class Op { kLn, kAddLn, kGather, kNormGather, kReverseAddLn, kAddNormGather, kLnAffine, kAddLnAffine };
 
 template <int C> struct Width;
@@ -765,19 +766,32 @@ using Streaming = Hints<true, true>;
 //    for the arithmetic: C = 384 add_ln -7%, add_ln_affine -5%,
 //    window_reverse_add_ln -1%, C = 192 ln_affine -2.5%. On the one-tile-per-
 //    wave kernels it cost up to 4% and is off.
+//  * C = 384 plain gather: K = 3 (16 lanes per row, 4 rows per wave
+//    instruction) capped at 4 workgroups per compute unit: -2 to -3% against
+//    K = 6 at one tile per wave; caps 2, 3, 5 and 8 and the pipelined loop
+//    measured equal or worse.
 //  * C = 768 and everything else: the default.
 template <int C, Op O> struct Launch {
     using H = Streaming;
     static constexpr int kBlocksPerCu = 0;
     static constexpr bool kPrefetch = false;
     static constexpr int kPriority = 0;
+    static constexpr int kChunks = 0;
 };
-template <int Cap, bool Prefetch, int Priority = 0> struct Tuned {
+template <int Cap, bool Prefetch, int Priority = 0, int Chunks = 0> struct Tuned {
     using H = Streaming;
     static constexpr int kBlocksPerCu = Cap;
     static constexpr bool kPrefetch = Prefetch;
     static constexpr int kPriority = Priority;
+    static constexpr int kChunks = Chunks;
 };
+// Chunks per lane of (width, op): the width's K unless the entry sets kChunks.
+// Only the plain gather may set it, as it copies bits and reduces nothing.
+// Every normalising kernel of a width keeps Width<C>::K, so they all reduce a
+// row in the same order.
+template <int C, Op O> constexpr int kChunksOf = Launch<C, O>::kChunks > 0 ? Launch<C, O>::kChunks : Width<C>::K;
+template <int C, Op O>
+constexpr bool kChunksOk = O == Op::kGather || kChunksOf<C, O> == Width<C>::K;
 template <> struct Launch<192, Op::kLn> : Tuned<0, true> {};
 template <> struct Launch<192, Op::kAddLn> : Tuned<0, true> {};
 template <> struct Launch<192, Op::kReverseAddLn> : Tuned<0, true> {};
@@ -785,6 +799,7 @@ template <> struct Launch<192, Op::kAddNormGather> : Tuned<0, true> {};
 template <> struct Launch<192, Op::kAddLnAffine> : Tuned<0, true> {};
 template <> struct Launch<384, Op::kLn> : Tuned<3, true> {};
 template <> struct Launch<384, Op::kNormGather> : Tuned<3, true> {};
+template <> struct Launch<384, Op::kGather> : Tuned<4, false, 0, 3> {};
 template <> struct Launch<384, Op::kAddLn> : Tuned<2, true, 1> {};
 template <> struct Launch<384, Op::kReverseAddLn> : Tuned<2, true, 1> {};
 template <> struct Launch<384, Op::kAddLnAffine> : Tuned<2, true, 1> {};
@@ -814,7 +829,8 @@ inline int compute_units() {
 
 template <int C, Op O>
 unsigned grid_for(int64_t rows) {
-    using T = Tile<C, Width<C>::K>;
+    static_assert(kChunksOk<C, O>, "a normalising kernel must use its width's chunk count");
+    using T = Tile<C, kChunksOf<C, O>>;
     const int64_t tiles = (rows + T::kRowsPerWave - 1) / T::kRowsPerWave;
     int64_t blocks = (tiles + (kBlock / 64) - 1) / (kBlock / 64);
     if (Launch<C, O>::kBlocksPerCu > 0) {
@@ -847,7 +863,7 @@ hipError_t gather_c(const void* x, int64_t n_src, const int32_t* table, int64_t 
                     void* out, hipStream_t s) {
     constexpr Op O = kNorm ? Op::kNormGather : Op::kGather;
     using L = Launch<C, O>;
-    gather_kernel<C, Width<C>::K, kNorm, typename L::H, L::kPrefetch><<<grid_for<C, O>(n_out), kBlock, 0, s>>>(
+    gather_kernel<C, kChunksOf<C, O>, kNorm, typename L::H, L::kPrefetch><<<grid_for<C, O>(n_out), kBlock, 0, s>>>(
         static_cast<const chunk_t*>(x), n_src, table, n_out, static_cast<chunk_t*>(out), eps);
     return hipGetLastError();
 }
