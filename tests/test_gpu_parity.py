@@ -216,6 +216,19 @@ def test_gather_out_of_range_entries_are_zero_rows(dev, C):
     assert not bits(ng[bad]).any()
 
 
+@pytest.mark.parametrize("C", [192, 384, 768])
+def test_gathers_loop_over_tiles_with_a_ragged_tail(dev, C):
+    # 49,157 output rows: more than two passes of the capped C = 384 grids
+    # (4 workgroups per CU x 4 waves x 4 rows for the plain gather, 3 x 4 x 8
+    # for norm_gather on 256 CUs), ending in a part-filled tile.
+    n_src, n_out = 20000, 49157
+    x = workloads.normal_rows(71, n_src, C, mean=0.2, std=1.7)
+    table = workloads.table_with_bad_entries(72, n_out, n_src)
+    tx, tt = to_dev(x, dev), to_dev(table, dev)
+    assert_bit_exact(host(lwg.window_gather(tx, tt)), oracle.window_gather(x, table), f"gather C={C} ragged")
+    assert_ln_close(host(lwg.norm_gather(tx, tt)), oracle.norm_gather(x, table), f"norm_gather C={C} ragged")
+
+
 def test_gather_id_encoded_rows(dev):
     grid = LEVEL2.grid
     n = LEVEL2.tokens
