@@ -219,21 +219,30 @@ __device__ __forceinline__ void layer_norm_lane(chunk_t (&v)[K], double eps) {
     }
 }
 
+// The 8 values of parameter chunk i, from LDS staged either as the binary16
+// chunks themselves or already widened to binary64 (8 doubles per chunk).
+__device__ __forceinline__ void param_chunk(const chunk_t* p, int i, double (&out)[8]) { unpack8(p[i], out); }
+__device__ __forceinline__ void param_chunk(const double* p, int i, double (&out)[8]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = p[8 * i + e];
+}
+
 // Affine LayerNorm: ((x - mean) / sqrt(var + eps)) * gamma + beta in binary64,
-// rounded once to binary16. gamma and beta are binary16 [C] (held in LDS by the
-// affine kernels); this lane reads its columns chunk by chunk as it writes them,
-// so only one chunk of them is live next to the row's deviations.
-template <int C, int K>
-__device__ __forceinline__ void layer_norm_affine_lane(chunk_t (&v)[K], const chunk_t* gamma,
-                                                       const chunk_t* beta, int sub, double eps) {
+// rounded once to binary16. gamma and beta are binary16 [C], held in LDS by the
+// affine kernels (as chunks, or widened: P); this lane reads its columns chunk
+// by chunk as it writes them, so only one chunk of them is live next to the
+// row's deviations.
+template <int C, int K, class P>
+__device__ __forceinline__ void layer_norm_affine_lane(chunk_t (&v)[K], const P* gamma,
+                                                       const P* beta, int sub, double eps) {
     using T = Tile<C, K>;
     double x[8 * K];
     const double rstd = row_stats<C, K>(v, x, eps);
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         double gk[8], bk[8];
-        unpack8(gamma[sub + k * T::kLanes], gk);
-        unpack8(beta[sub + k * T::kLanes], bk);
+        param_chunk(gamma, sub + k * T::kLanes, gk);
+        param_chunk(beta, sub + k * T::kLanes, bk);
         const double* xk = x + 8 * k;
         v[k] = chunk_t{pack2(__builtin_fma(xk[0] * rstd, gk[0], bk[0]), __builtin_fma(xk[1] * rstd, gk[1], bk[1])),
                        pack2(__builtin_fma(xk[2] * rstd, gk[2], bk[2]), __builtin_fma(xk[3] * rstd, gk[3], bk[3])),
@@ -379,11 +388,19 @@ __global__ __launch_bounds__(kBlock) void add_ln_kernel(const chunk_t* branch, c
 }
 
 // Affine LayerNorm and residual add + affine LayerNorm. gamma and beta are
-// binary16 [C]; each workgroup copies them once into LDS (2*C*2 bytes, at most
-// 3 KB) and every lane reads its columns from there chunk by chunk, so the
-// parameters neither occupy the vector-memory path nor sit widened in
-// registers. y may alias x, and residual_out / y may alias the inputs as in the
-// plain kernels.
+// binary16 [C]; each workgroup copies them once into LDS and every lane reads
+// its columns from there chunk by chunk, so the parameters neither occupy the
+// vector-memory path nor sit widened in registers. kWide selects the LDS form:
+// the binary16 chunks (2*C*2 bytes; each use converts 16 values to binary64),
+// or values widened to binary64 as they are staged (2*C*8 bytes, at most
+// 12 KB; each use is a plain LDS read). y may alias x, and residual_out / y may
+// alias the inputs as in the plain kernels.
+template <int C, bool kWide>
+struct AffineStage {
+    using P = std::conditional_t<kWide, double, chunk_t>;
+    static constexpr int kHalf = kWide ? C : C / 8;     // entries of gamma (and of beta)
+};
+
 template <int C>
 __device__ __forceinline__ void stage_params(chunk_t* params, const chunk_t* gamma, const chunk_t* beta) {
     constexpr int kChunks = C / 8;
@@ -392,15 +409,28 @@ __device__ __forceinline__ void stage_params(chunk_t* params, const chunk_t* gam
     __syncthreads();
 }
 
-template <int C, int K, class H, int kPrio>
+template <int C>
+__device__ __forceinline__ void stage_params(double* params, const chunk_t* gamma, const chunk_t* beta) {
+    constexpr int kChunks = C / 8;
+    for (int i = threadIdx.x; i < 2 * kChunks; i += kBlock) {
+        double v[8];
+        unpack8(i < kChunks ? gamma[i] : beta[i - kChunks], v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) params[8 * i + e] = v[e];
+    }
+    __syncthreads();
+}
+
+template <int C, int K, class H, int kPrio, bool kWide>
 __global__ __launch_bounds__(kBlock) void ln_affine_kernel(const chunk_t* x, const chunk_t* gamma,
                                                            const chunk_t* beta, chunk_t* y,
                                                            int64_t rows, double eps) {
     using T = Tile<C, K>;
-    __shared__ chunk_t params[2 * T::kChunks];
+    using S = AffineStage<C, kWide>;
+    __shared__ typename S::P params[2 * S::kHalf];
     stage_params<C>(params, gamma, beta);
-    gamma = params;
-    beta = params + T::kChunks;
+    const typename S::P* gamma_s = params;
+    const typename S::P* beta_s = params + S::kHalf;
     const int lane = threadIdx.x & 63;
     const int sub = lane % T::kLanes;
     const int64_t stride = wave_stride();
@@ -411,22 +441,23 @@ __global__ __launch_bounds__(kBlock) void ln_affine_kernel(const chunk_t* x, con
         // re-read gamma/beta from LDS per row tile instead of letting the
         // compiler hoist 2*K widened chunks out of the loop into registers
         asm volatile("" ::: "memory");
-        layer_norm_affine_lane<C, K>(v, gamma, beta, sub, eps);
+        layer_norm_affine_lane<C, K>(v, gamma_s, beta_s, sub, eps);
         store_tile<C, K, H>(y, w, rows, lane, v);
         load_tile<C, K, H, kPrio>(x, w + stride, rows, lane, v);
     }
 }
 
-template <int C, int K, class H, bool kPrefetch, int kPrio>
+template <int C, int K, class H, bool kPrefetch, int kPrio, bool kWide>
 __global__ __launch_bounds__(kBlock) void add_ln_affine_kernel(const chunk_t* branch, const chunk_t* residual,
                                                                  const chunk_t* gamma, const chunk_t* beta,
                                                                  chunk_t* residual_out, chunk_t* y,
                                                                  int64_t rows, double eps) {
     using T = Tile<C, K>;
-    __shared__ chunk_t params[2 * T::kChunks];
+    using S = AffineStage<C, kWide>;
+    __shared__ typename S::P params[2 * S::kHalf];
     stage_params<C>(params, gamma, beta);
-    gamma = params;
-    beta = params + T::kChunks;
+    const typename S::P* gamma_s = params;
+    const typename S::P* beta_s = params + S::kHalf;
     const int lane = threadIdx.x & 63;
     const int sub = lane % T::kLanes;
     const int64_t stride = wave_stride();
@@ -443,7 +474,7 @@ __global__ __launch_bounds__(kBlock) void add_ln_affine_kernel(const chunk_t* br
         asm volatile("" ::: "memory");  // as in ln_affine_kernel: no hoisting of gamma/beta
         residual_add<K>(b, r);
         store_tile<C, K, H>(residual_out, w, rows, lane, r);
-        layer_norm_affine_lane<C, K>(r, gamma, beta, sub, eps);
+        layer_norm_affine_lane<C, K>(r, gamma_s, beta_s, sub, eps);
         store_tile<C, K, H>(y, w, rows, lane, r);
         if constexpr (kPrefetch) {
 #pragma unroll
@@ -739,11 +770,15 @@ __global__ __launch_bounds__(kBlock) void bias_gelu_kernel(const f32x4_t* x, con
 enum class Op { kLn, kAddLn, kGather, kNormGather, kReverseAddLn, kAddNormGather, kLnAffine, kAddLnAffine };
 
 template <int C> struct Width;
-template <> struct Width<192> { static constexpr int K = 3; };
-template <> struct Width<384> { static constexpr int K = 6; };
+// kWideParams: the affine kernels stage gamma and beta in LDS widened to
+// binary64. Measured against binary16 staging: C = 384 ln_affine -2.8%,
+// add_ln_affine -2.1%; C = 192 +1.2% / +1.0% and C = 768 ln_affine +4.3%, so
+// only C = 384 takes it.
+template <> struct Width<192> { static constexpr int K = 3; static constexpr bool kWideParams = false; };
+template <> struct Width<384> { static constexpr int K = 6; static constexpr bool kWideParams = true; };
 // the patch-merge width: 16 lanes per row, 6 chunks each (whole 256-byte pieces
 // of 4 rows per wave instruction)
-template <> struct Width<768> { static constexpr int K = 6; };
+template <> struct Width<768> { static constexpr int K = 6; static constexpr bool kWideParams = false; };
 
 using Streaming = Hints<true, true>;
 
@@ -952,7 +987,8 @@ template <int C>
 hipError_t ln_affine_c(const void* x, const void* g, const void* b, void* y, int64_t rows, double eps,
                        hipStream_t s) {
     using L = Launch<C, Op::kLnAffine>;
-    ln_affine_kernel<C, Width<C>::K, typename L::H, L::kPriority><<<grid_for<C, Op::kLnAffine>(rows), kBlock, 0, s>>>(
+    ln_affine_kernel<C, Width<C>::K, typename L::H, L::kPriority, Width<C>::kWideParams>
+        <<<grid_for<C, Op::kLnAffine>(rows), kBlock, 0, s>>>(
         static_cast<const chunk_t*>(x), static_cast<const chunk_t*>(g), static_cast<const chunk_t*>(b),
         static_cast<chunk_t*>(y), rows, eps);
     return hipGetLastError();
@@ -967,7 +1003,7 @@ template <int C>
 hipError_t add_ln_affine_c(const void* br, const void* r, const void* g, const void* b, void* ro, void* y,
                            int64_t rows, double eps, hipStream_t s) {
     using L = Launch<C, Op::kAddLnAffine>;
-    add_ln_affine_kernel<C, Width<C>::K, typename L::H, L::kPrefetch, L::kPriority>
+    add_ln_affine_kernel<C, Width<C>::K, typename L::H, L::kPrefetch, L::kPriority, Width<C>::kWideParams>
         <<<grid_for<C, Op::kAddLnAffine>(rows), kBlock, 0, s>>>(
             static_cast<const chunk_t*>(br), static_cast<const chunk_t*>(r), static_cast<const chunk_t*>(g),
             static_cast<const chunk_t*>(b), static_cast<chunk_t*>(ro), static_cast<chunk_t*>(y), rows, eps);
