@@ -787,12 +787,15 @@ using Streaming = Hints<true, true>;
 // row loop (the next tile's loads issued before the current tile is
 // normalised). Each entry was measured against the alternatives on cold
 // buffers, in interleaved runs on one MI355X:
-//  * C = 384: the pipelined single-input kernels hold 150-160 VGPRs (3 waves
-//    per SIMD) and the two-input ones 190-194 (2 waves); a cap that fills
-//    exactly those slots lets each wave take 1.3-2.3 tiles and normalise one
-//    while the next loads: ln_fixed -11%, norm_gather -10%, add_ln -4%,
-//    window_reverse_add_ln -4%, add_ln_affine -6%. ln_affine gains 9% from the
-//    cap alone and add_norm_gather 1% (both lose with the pipeline).
+//  * C = 384: with a cap each wave takes 1.3-2.3 tiles and, pipelined,
+//    normalises one while the next loads: ln_fixed -11%, norm_gather -10%,
+//    add_ln -4%, window_reverse_add_ln -4%, add_ln_affine -6%; ln_affine gains
+//    9% from the cap alone (it loses with the pipeline). The single-input
+//    pipelined kernels hold 136-140 VGPRs (3 waves per SIMD) and take cap 3.
+//    The two-input ones hold 168-180 and take cap 2: caps 3 and 4 measured
+//    3-16% slower, although 3 waves of 168 VGPRs would fit. add_norm_gather
+//    (117 VGPRs) is fastest pipelined at cap 4: -3.4% against cap 2 without
+//    the pipeline.
 //  * C = 192, one tile per wave: the pipelined form of ln_fixed, add_ln and the
 //    fused residual kernels issues the tile's loads ahead of the loop test and
 //    measured 2-4% faster; the gathers and ln_affine are fastest as they are.
@@ -840,7 +843,7 @@ template <> struct Launch<384, Op::kReverseAddLn> : Tuned<2, true, 1> {};
 template <> struct Launch<384, Op::kAddLnAffine> : Tuned<2, true, 1> {};
 template <> struct Launch<384, Op::kLnAffine> : Tuned<3, false> {};
 template <> struct Launch<192, Op::kLnAffine> : Tuned<0, false, 1> {};
-template <> struct Launch<384, Op::kAddNormGather> : Tuned<2, false> {};
+template <> struct Launch<384, Op::kAddNormGather> : Tuned<4, true> {};
 
 
 // Compute units of the device, queried on first use (0 = not yet known). Only
