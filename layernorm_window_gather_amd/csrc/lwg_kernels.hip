@@ -808,7 +808,10 @@ using Streaming = Hints<true, true>;
 //    instruction) capped at 4 workgroups per compute unit: -2 to -3% against
 //    K = 6 at one tile per wave; caps 2, 3, 5 and 8 and the pipelined loop
 //    measured equal or worse.
-//  * C = 768 and everything else: the default.
+//  * C = 768: ln_fixed (109 VGPRs) pipelined at cap 3, -3.4 to -4.5% (cap 2
+//    +1%, cap 4 +10%, uncapped -2%); ln_affine at one tile per wave with load
+//    priority, -1.1 to -1.4% (caps 2-4 +3 to +10%).
+//  * Everything else: the default.
 template <int C, Op O> struct Launch {
     using H = Streaming;
     static constexpr int kBlocksPerCu = 0;
@@ -844,6 +847,8 @@ template <> struct Launch<384, Op::kAddLnAffine> : Tuned<2, true, 1> {};
 template <> struct Launch<384, Op::kLnAffine> : Tuned<3, false> {};
 template <> struct Launch<192, Op::kLnAffine> : Tuned<0, false, 1> {};
 template <> struct Launch<384, Op::kAddNormGather> : Tuned<4, true> {};
+template <> struct Launch<768, Op::kLn> : Tuned<3, true> {};
+template <> struct Launch<768, Op::kLnAffine> : Tuned<0, false, 1> {};
 
 
 // Compute units of the device, queried on first use (0 = not yet known). Only
