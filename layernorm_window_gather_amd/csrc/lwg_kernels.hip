@@ -266,13 +266,20 @@ __device__ __forceinline__ void zero(chunk_t (&v)[K]) {
 // The launcher sizes the grid either to one tile per wave or to a fixed number
 // of resident workgroups.
 
-__device__ __forceinline__ int64_t first_wave() {
-    return static_cast<int64_t>(blockIdx.x) * (kBlock / 64) + (threadIdx.x >> 6);
+template <int kWaves>
+__device__ __forceinline__ int64_t first_wave_in() {
+    return static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
 }
 
-__device__ __forceinline__ int64_t wave_stride() {
-    return static_cast<int64_t>(gridDim.x) * (kBlock / 64);
+template <int kWaves>
+__device__ __forceinline__ int64_t wave_stride_in() {
+    return static_cast<int64_t>(gridDim.x) * kWaves;
 }
+
+// For kernels launched with kBlock threads per workgroup (all but the gathers,
+// whose workgroup size is a launch-table choice).
+__device__ __forceinline__ int64_t first_wave() { return first_wave_in<kBlock / 64>(); }
+__device__ __forceinline__ int64_t wave_stride() { return wave_stride_in<kBlock / 64>(); }
 
 // The K chunks this lane holds of row tile w (zeros past the last row). With
 // kPrio > 0 the wave issues the loads at that scheduling priority (s_setprio)
@@ -506,16 +513,16 @@ __device__ __forceinline__ void load_gathered(const chunk_t* x, int64_t n_src, c
     }
 }
 
-template <int C, int K, bool kNorm, class H, bool kPrefetch>
-__global__ __launch_bounds__(kBlock) void gather_kernel(const chunk_t* __restrict__ x, int64_t n_src,
-                                                        const int32_t* __restrict__ table,
-                                                        int64_t n_out, chunk_t* __restrict__ out,
-                                                        double eps) {
+template <int C, int K, bool kNorm, class H, bool kPrefetch, int kWaves>
+__global__ __launch_bounds__(64 * kWaves) void gather_kernel(const chunk_t* __restrict__ x, int64_t n_src,
+                                                             const int32_t* __restrict__ table,
+                                                             int64_t n_out, chunk_t* __restrict__ out,
+                                                             double eps) {
     using T = Tile<C, K>;
     const int lane = threadIdx.x & 63;
     if constexpr (kPrefetch) {
-        const int64_t stride = wave_stride();
-        int64_t w = first_wave();
+        const int64_t stride = wave_stride_in<kWaves>();
+        int64_t w = first_wave_in<kWaves>();
         chunk_t v[K];
         load_gathered<C, K, H>(x, n_src, table, n_out, w, lane, v);
         for (; w * T::kRowsPerWave < n_out; w += stride) {
@@ -528,7 +535,7 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(const chunk_t* __restric
         }
     } else {
         const int sub = lane % T::kLanes;
-        for (int64_t w = first_wave(); w * T::kRowsPerWave < n_out; w += wave_stride()) {
+        for (int64_t w = first_wave_in<kWaves>(); w * T::kRowsPerWave < n_out; w += wave_stride_in<kWaves>()) {
             const int64_t j = w * T::kRowsPerWave + lane / T::kLanes;
             const bool live = j < n_out;
             const int32_t t = live ? table[j] : -1;
@@ -804,6 +811,12 @@ using Streaming = Hints<true, true>;
 //    for the arithmetic: C = 384 add_ln -7%, add_ln_affine -5%,
 //    window_reverse_add_ln -1%, C = 192 ln_affine -2.5%. On the one-tile-per-
 //    wave kernels it cost up to 4% and is off.
+//  * C = 384 norm_gather runs one wave per workgroup, 12 workgroups per
+//    compute unit (the same 12 waves as 3 four-wave workgroups): -1.9%. Caps
+//    of 8, 16 and 24 one-wave workgroups, the loop without the pipeline, and
+//    one tile per wave measured 6-16% slower. (Numbering the waves across
+//    workgroups, so that neighbouring tiles land on different XCDs, was 3-30%
+//    slower on every kernel.)
 //  * C = 384 plain gather: K = 3 (16 lanes per row, 4 rows per wave
 //    instruction) capped at 4 workgroups per compute unit: -2 to -3% against
 //    K = 6 at one tile per wave; caps 2, 3, 5 and 8 and the pipelined loop
@@ -818,13 +831,15 @@ template <int C, Op O> struct Launch {
     static constexpr bool kPrefetch = false;
     static constexpr int kPriority = 0;
     static constexpr int kChunks = 0;
+    static constexpr int kWaves = kBlock / 64;
 };
-template <int Cap, bool Prefetch, int Priority = 0, int Chunks = 0> struct Tuned {
+template <int Cap, bool Prefetch, int Priority = 0, int Chunks = 0, int Waves = kBlock / 64> struct Tuned {
     using H = Streaming;
     static constexpr int kBlocksPerCu = Cap;
     static constexpr bool kPrefetch = Prefetch;
     static constexpr int kPriority = Priority;
     static constexpr int kChunks = Chunks;
+    static constexpr int kWaves = Waves;       // waves per workgroup (gathers only)
 };
 // Chunks per lane of (width, op): the width's K unless the entry sets kChunks.
 // Only the plain gather may set it, as it copies bits and reduces nothing.
@@ -839,7 +854,7 @@ template <> struct Launch<192, Op::kReverseAddLn> : Tuned<0, true> {};
 template <> struct Launch<192, Op::kAddNormGather> : Tuned<0, true> {};
 template <> struct Launch<192, Op::kAddLnAffine> : Tuned<0, true> {};
 template <> struct Launch<384, Op::kLn> : Tuned<3, true> {};
-template <> struct Launch<384, Op::kNormGather> : Tuned<3, true> {};
+template <> struct Launch<384, Op::kNormGather> : Tuned<12, true, 0, 0, 1> {};
 template <> struct Launch<384, Op::kGather> : Tuned<4, false, 0, 3> {};
 template <> struct Launch<384, Op::kAddLn> : Tuned<2, true, 1> {};
 template <> struct Launch<384, Op::kReverseAddLn> : Tuned<2, true, 1> {};
@@ -873,9 +888,12 @@ inline int compute_units() {
 template <int C, Op O>
 unsigned grid_for(int64_t rows) {
     static_assert(kChunksOk<C, O>, "a normalising kernel must use its width's chunk count");
+    static_assert(O == Op::kGather || O == Op::kNormGather || Launch<C, O>::kWaves == kBlock / 64,
+                  "only the gathers take their workgroup size from the launch table");
     using T = Tile<C, kChunksOf<C, O>>;
+    constexpr int kWaves = Launch<C, O>::kWaves;
     const int64_t tiles = (rows + T::kRowsPerWave - 1) / T::kRowsPerWave;
-    int64_t blocks = (tiles + (kBlock / 64) - 1) / (kBlock / 64);
+    int64_t blocks = (tiles + kWaves - 1) / kWaves;
     if (Launch<C, O>::kBlocksPerCu > 0) {
         const int64_t cap = static_cast<int64_t>(compute_units()) * Launch<C, O>::kBlocksPerCu;
         if (blocks > cap) blocks = cap;
@@ -906,7 +924,8 @@ hipError_t gather_c(const void* x, int64_t n_src, const int32_t* table, int64_t 
                     void* out, hipStream_t s) {
     constexpr Op O = kNorm ? Op::kNormGather : Op::kGather;
     using L = Launch<C, O>;
-    gather_kernel<C, kChunksOf<C, O>, kNorm, typename L::H, L::kPrefetch><<<grid_for<C, O>(n_out), kBlock, 0, s>>>(
+    gather_kernel<C, kChunksOf<C, O>, kNorm, typename L::H, L::kPrefetch, L::kWaves>
+        <<<grid_for<C, O>(n_out), 64 * L::kWaves, 0, s>>>(
         static_cast<const chunk_t*>(x), n_src, table, n_out, static_cast<chunk_t*>(out), eps);
     return hipGetLastError();
 }
