@@ -26,10 +26,13 @@ and the window reverse that follows attention, plus the two fusions around it:
 
 and, for callers that keep the LayerNorm scale and shift:
   ln_affine(x, gamma, beta), add_ln_affine(branch, residual, gamma, beta)
-Widths: 192 and 384 (the model's), 768 (its patch-merge width).
 
 and the float32 bias + tanh-GELU of the HIP extension tutorial:
   bias_gelu(x, bias)                 gelu_tanh(x + bias), float32
+
+Row widths: 192 and 384 (the model's) and 768 (its patch-merge width).
+prepare(op, ...) checks the arguments once and returns a callable that only
+crosses the C ABI (for timing loops).
 """
 from __future__ import annotations
 
@@ -40,10 +43,12 @@ import torch
 from . import _lib
 from ._lib import LwgError
 
-__all__ = ["ln_fixed", "add_ln", "ln_affine", "add_ln_affine", "bias_gelu", "window_token_count", "window_index_build", "window_table",
-           "window_gather", "norm_gather", "window_inverse_build", "window_inverse_table",
-           "window_reverse", "window_reverse_add_ln", "add_norm_gather", "LwgError", "WIDTHS", "EPS",
-           "library"]
+__all__ = [
+    "ln_fixed", "add_ln", "window_token_count", "window_index_build", "window_table", "window_gather",
+    "norm_gather", "window_inverse_build", "window_inverse_table", "window_reverse", "window_reverse_add_ln",
+    "add_norm_gather", "ln_affine", "add_ln_affine", "bias_gelu", "prepare", "library", "LwgError", "WIDTHS",
+    "EPS",
+]
 
 WIDTHS = (192, 384, 768)
 EPS = 1e-5
