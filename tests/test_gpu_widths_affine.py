@@ -171,3 +171,32 @@ def test_every_layernorm_rounds_once_next_to_a_midpoint(dev, C):
         got = host(y)
         assert_bit_exact(got[crafted], ref[crafted], f"{name} C={C} next to the midpoint")
         assert_ln_close(got, ref, f"{name} C={C}")
+
+
+@pytest.mark.parametrize("C", [192, 384, 768])
+def test_subnormal_inputs_and_outputs(dev, C):
+    """Rows of binary16 subnormals (|x| < 2**-14, spacing 2**-24) with eps = 0.5:
+    the variance is far below eps, so y ~ 1.4 (x - mean) lands in the binary16
+    subnormal range too. Every normalising kernel must return the oracle's
+    binary16 values bit for bit: subnormal inputs widen exactly, and subnormal
+    outputs are produced, not flushed to zero."""
+    rng = np.random.default_rng(800 + C)
+    n = 333
+    x = (rng.integers(-1023, 1024, size=(n, C)) * 2.0 ** -24).astype(np.float16)   # subnormals and zeros
+    assert np.all(np.abs(x.astype(np.float64)) < 2.0 ** -14)
+    eps = 0.5
+    ref = oracle.layer_norm(x, eps)
+    sub = (ref != 0) & (np.abs(ref.astype(np.float64)) < 2.0 ** -14)
+    assert sub.mean() > 0.5                     # most outputs are subnormal
+    xd, zd = to_dev(x, dev), torch.zeros(n, C, dtype=torch.float16, device=dev)
+    ones, zeros = np.ones(C, np.float16), np.zeros(C, np.float16)
+    ident = torch.arange(n, dtype=torch.int32, device=dev)
+    outs = {
+        "ln_fixed": lwg.ln_fixed(xd, eps),
+        "add_ln": lwg.add_ln(xd, zd, eps)[1],
+        "norm_gather": lwg.norm_gather(xd, ident, eps),
+        "add_norm_gather": lwg.add_norm_gather(xd, zd, ident, eps)[1],
+        "ln_affine": lwg.ln_affine(xd, to_dev(ones, dev), to_dev(zeros, dev), eps),
+    }
+    for name, y in outs.items():
+        assert_bit_exact(host(y), ref, f"{name} C={C} subnormal rows")
