@@ -200,3 +200,27 @@ def test_subnormal_inputs_and_outputs(dev, C):
     }
     for name, y in outs.items():
         assert_bit_exact(host(y), ref, f"{name} C={C} subnormal rows")
+
+
+@pytest.mark.parametrize("C", [192, 384, 768])
+def test_affine_output_at_the_binary16_overflow_threshold(dev, C):
+    """gamma = 65504 and a +-1 row with eps = 1e-12 give y = +-(1 - 5e-13), so
+    y * gamma + beta lies 3.3e-8 below 65520 (the threshold where binary16
+    rounds to +Inf) for beta = 16 and just above it for beta = 17. A single
+    rounding gives 65504 and +Inf; a binary32 value first would round the
+    beta = 16 case up to 65520 and then to +Inf. The negative side lands
+    between binary16 neighbours and goes to -65472."""
+    n, half = 6, C // 2
+    pm = np.array([1.0] * half + [-1.0] * half, dtype=np.float16)
+    x = np.stack([pm, pm[::-1], pm, np.roll(pm, 3), pm, pm]).astype(np.float16)[:n]
+    gamma = np.full(C, 65504.0, np.float16)
+    beta = np.where(np.arange(C) % 2 == 0, 16.0, 17.0).astype(np.float16)
+    eps = 1e-12
+    ref = oracle.layer_norm_affine(x, gamma, beta, eps)
+    r0 = bits(ref[0])
+    assert np.all(r0[:half][0::2] == 0x7BFF) and np.all(r0[:half][1::2] == 0x7C00)   # 65504, +Inf
+    assert np.all(r0[half:] == 0xFBFE)                                                 # -65472
+    xd, tg, tb = to_dev(x, dev), to_dev(gamma, dev), to_dev(beta, dev)
+    assert_bit_exact(host(lwg.ln_affine(xd, tg, tb, eps)), ref, f"ln_affine C={C} at the overflow threshold")
+    r, y = lwg.add_ln_affine(xd, torch.zeros_like(xd), tg, tb, eps)
+    assert_bit_exact(host(y), ref, f"add_ln_affine C={C} at the overflow threshold")
