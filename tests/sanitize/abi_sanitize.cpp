@@ -196,6 +196,6 @@ int main(int argc, char** argv) {
     fixed_cases();
     sweep(iterations);
     std::printf("abi_sanitize: %ld launches reached, %ld launcher precondition violations, %d failures\n",
-                stubs::g_launches, stubs::g_violations, g_failures);
+                stubs::g_launches.load(), stubs::g_violations.load(), g_failures);
     return (g_failures == 0 && stubs::g_violations == 0) ? 0 : 1;
 }

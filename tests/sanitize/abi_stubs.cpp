@@ -11,8 +11,8 @@
 #include "abi_stubs.h"
 
 namespace stubs {
-long g_launches = 0;
-long g_violations = 0;
+std::atomic<long> g_launches{0};
+std::atomic<long> g_violations{0};
 }  // namespace stubs
 
 namespace {
