@@ -388,6 +388,45 @@ def test_runs_on_the_callers_stream(dev):
     assert_ln_close(y2.cpu().numpy(), oracle.layer_norm(oracle.layer_norm(x)), "chained on side stream")
 
 
+def test_two_streams_at_once(dev):
+    # The kernels keep no state between calls, so work on two streams may run
+    # concurrently: each stream chains add_ln -> norm_gather -> ln_fixed on its
+    # own buffers (level-1 width on one, level-2 width on the other), issued
+    # interleaved, and each result must match the oracle.
+    streams = [torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)]
+    cases = []
+    for k, (grid, C) in enumerate((((4, 30, 40), 192), ((4, 15, 20), 384))):
+        n = int(np.prod(grid))
+        br = workloads.normal_rows(900 + k, n, C)
+        res = workloads.normal_rows(910 + k, n, C, std=0.5)
+        cases.append((grid, C, br, res))
+    torch.cuda.synchronize(dev)
+    outs = []
+    for s, (grid, C, br, res) in zip(streams, cases):
+        with torch.cuda.stream(s):
+            tb, tr = to_dev(br, dev), to_dev(res, dev)
+            table = lwg.window_index_build(grid, WINDOW, SHIFT, device=dev)
+            outs.append([tb, tr, table])
+    for rep in range(3):                 # interleave the two streams' launches
+        for s, o in zip(streams, outs):
+            with torch.cuda.stream(s):
+                tb, tr, table = o[:3]
+                r, y = lwg.add_ln(tb, tr, residual_out=tr)
+                g = lwg.norm_gather(r, table)
+                z = lwg.ln_fixed(y)
+                o[3:] = [g, z]
+    for s in streams:
+        s.synchronize()
+    for (grid, C, br, res), o in zip(cases, outs):
+        table = oracle.window_index_table(grid, WINDOW, SHIFT)
+        r = res
+        for _ in range(3):
+            r, y = oracle.add_ln(br, r)
+        assert_bit_exact(host(o[1]), r, f"two streams: residual C={C}")
+        assert_ln_close(host(o[3]), oracle.norm_gather(r, table), f"two streams: norm_gather C={C}")
+        assert_ln_close(host(o[4]), oracle.layer_norm(y), f"two streams: ln_fixed C={C}")
+
+
 def test_cached_tables_built_on_one_stream_serve_another(dev):
     """A cached table first built on a side stream is complete when the call
     returns, and gathers on the default stream read it correctly."""
