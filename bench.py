@@ -289,12 +289,17 @@ def next_ops_gate(lwg, torch, dev, host, levels):
 
 
 SWEEP_ROWS = (16384, 32768, 65536, 131040, 262144, 524288)
+# grids of the C = 384 gather sweep: level 2's 8 x _ x 45 with the grid height varied
+# (32760 tokens at height 91), cut by the (2, 6, 12) window with shift (1, 3, 6)
+GATHER_SWEEP_GRIDS = ((8, 12, 45), (8, 24, 45), (8, 48, 45), (8, 91, 45), (8, 182, 45), (8, 364, 45))
 
 
 def size_sweep(lwg, torch, dev, reps):
-    """add_ln and ln_fixed at C = 192 over SWEEP_ROWS, each on a cold buffer pool,
-    timed like the per-kernel table; a least-squares fit of time = fixed + bytes /
-    rate separates the per-launch fixed cost from the streaming rate."""
+    """add_ln and ln_fixed at C = 192 over SWEEP_ROWS, and norm_gather,
+    window_gather and ln_fixed at C = 384 over GATHER_SWEEP_GRIDS, each on a cold
+    buffer pool, timed like the per-kernel table; a least-squares fit of time =
+    fixed + bytes / rate separates the per-launch fixed cost from the streaming
+    rate."""
     c = 192
     base = workloads.normal_rows(9, 1 << 16, c)
     out = {"C": c, "rows": list(SWEEP_ROWS), "add_ln_us": [], "ln_fixed_us": [], "torch_copy_us": []}
@@ -334,14 +339,47 @@ def size_sweep(lwg, torch, dev, reps):
             out[f"{op}_us"].append(round(timed(pool), 3))
             del pool
             torch.cuda.empty_cache()
-    fit = {}
-    for op, per_row in (("add_ln", 4 * c * HALF), ("ln_fixed", 2 * c * HALF), ("torch_copy", 2 * c * HALF)):
-        nb = np.array([r * per_row for r in SWEEP_ROWS], dtype=np.float64)
-        us = np.array(out[f"{op}_us"])
+    def fit_of(nbytes, us):
+        nb = np.array(nbytes, dtype=np.float64)
+        us = np.array(us)
         (fixed, slope), *_ = np.linalg.lstsq(np.vstack([np.ones_like(nb), nb]).T, us, rcond=None)
-        fit[op] = {"fixed_us": round(float(fixed), 2), "marginal_GBps": round(1e-3 / float(slope), 1),
-                   "pct_of_peak_at_sizes": [round(100 * b / (t * 1e3) / PEAK_GBS, 1) for b, t in zip(nb, us)]}
-    out["fit"] = fit
+        return {"fixed_us": round(float(fixed), 2), "marginal_GBps": round(1e-3 / float(slope), 1),
+                "pct_of_peak_at_sizes": [round(100 * b / (t * 1e3) / PEAK_GBS, 1) for b, t in zip(nb, us)]}
+
+    out["fit"] = {op: fit_of([r * per_row for r in SWEEP_ROWS], out[f"{op}_us"])
+                  for op, per_row in (("add_ln", 4 * c * HALF), ("ln_fixed", 2 * c * HALF),
+                                      ("torch_copy", 2 * c * HALF))}
+
+    # C = 384: the gathers against ln_fixed over the same token counts, in the
+    # level-2 launch configuration; their extra per-launch cost is the fixed term
+    c = 384
+    base = workloads.normal_rows(10, 1 << 15, c)
+    g = {"C": c, "grids": [list(gr) for gr in GATHER_SWEEP_GRIDS], "tokens": [], "rows_out": [],
+         "norm_gather_us": [], "window_gather_us": [], "ln_fixed_us": [], "bytes": {}}
+    nbytes = {"norm_gather": [], "window_gather": [], "ln_fixed": []}
+    for grid in GATHER_SWEEP_GRIDS:
+        n = int(np.prod(grid))
+        m = lwg.window_token_count(grid, WINDOW)
+        g["tokens"].append(n)
+        g["rows_out"].append(m)
+        x0 = torch.from_numpy(np.resize(base, (n, c))).to(dev)
+        table = lwg.window_index_build(grid, WINDOW, SHIFT, device=dev)
+        for op in ("norm_gather", "window_gather", "ln_fixed"):
+            nb = algorithmic_bytes(op, n, m, c)
+            nbytes[op].append(nb)
+            count = max(3, -(-COLD_BYTES // nb) + 1)
+            if op == "ln_fixed":
+                pool = [lwg.prepare(op, xx, torch.empty_like(xx)) for xx in (x0.clone() for _ in range(count))]
+            else:
+                pool = [lwg.prepare(op, x0.clone(), table, torch.empty(m, c, dtype=torch.float16, device=dev))
+                        for _ in range(count)]
+            g[f"{op}_us"].append(round(timed(pool), 3))
+            del pool
+            torch.cuda.empty_cache()
+        del x0, table
+    g["bytes"] = nbytes
+    g["fit"] = {op: fit_of(nbytes[op], g[f"{op}_us"]) for op in nbytes}
+    out["gathers_c384"] = g
     return out
 
 
