@@ -484,7 +484,8 @@ def main(argv=None):
     ap.add_argument("--only", choices=OPS + NEXT_OPS + ("all",), default=None,
                     help="launch only this op (or every op), --steps times per level (profiling runs)")
     ap.add_argument("--size-sweep", action="store_true",
-                    help="time add_ln and ln_fixed at C=192 over a range of row counts and fit fixed cost + rate")
+                    help="time add_ln and ln_fixed at C=192, and the gathers against ln_fixed at C=384, "
+                         "over a range of sizes and fit fixed cost + rate")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="also run an elementwise copy of this many MiB (PMC calibration)")
     args = ap.parse_args(argv)
