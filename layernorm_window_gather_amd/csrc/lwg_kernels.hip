@@ -865,6 +865,28 @@ template <> struct Launch<384, Op::kAddNormGather> : Tuned<4, true> {};
 template <> struct Launch<768, Op::kLn> : Tuned<3, true> {};
 template <> struct Launch<768, Op::kLnAffine> : Tuned<0, false, 1> {};
 
+// The caps above were chosen at the model's sizes, where each wave of a capped
+// grid takes 1.1-2.3 row tiles. On larger inputs a capped grid makes every wave
+// loop over many tiles, and one tile per wave streams better. A capped entry
+// keeps its cap only while its waves would take at most kMaxTilesPerWave tiles
+// each (0 = always). Measured at C = 384 on 65,520 and 131,040 tokens (grids
+// 8 x 182 x 45 and 8 x 364 x 45), cap against one tile per wave: at 131,040 one
+// tile per wave was 1-10% faster for every kernel; at 65,520 it was faster
+// for norm_gather (-4.4%) and add_norm_gather (-6.0%) at 2.9 and 2.2 tiles per
+// wave, and for add_ln, window_reverse_add_ln and add_ln_affine (-3 to -7%) at
+// 4 tiles per wave, but slower for ln_fixed (+2.0%, 2.7 tiles per wave) and
+// the plain gather (+1.2%, 4.4 tiles per wave). C = 768 was only measured at
+// its workload size and keeps its cap.
+template <int C, Op O> constexpr int kMaxTilesPerWave = 0;
+template <> constexpr int kMaxTilesPerWave<384, Op::kLn> = 3;
+template <> constexpr int kMaxTilesPerWave<384, Op::kAddLn> = 3;
+template <> constexpr int kMaxTilesPerWave<384, Op::kReverseAddLn> = 3;
+template <> constexpr int kMaxTilesPerWave<384, Op::kAddLnAffine> = 3;
+template <> constexpr int kMaxTilesPerWave<384, Op::kLnAffine> = 3;
+template <> constexpr int kMaxTilesPerWave<384, Op::kNormGather> = 2;
+template <> constexpr int kMaxTilesPerWave<384, Op::kAddNormGather> = 2;
+template <> constexpr int kMaxTilesPerWave<384, Op::kGather> = 5;
+
 
 // Compute units of the device, queried on first use (0 = not yet known). Only
 // the launch shape of capped grids depends on it, never a result; a failed
@@ -896,7 +918,8 @@ unsigned grid_for(int64_t rows) {
     int64_t blocks = (tiles + kWaves - 1) / kWaves;
     if (Launch<C, O>::kBlocksPerCu > 0) {
         const int64_t cap = static_cast<int64_t>(compute_units()) * Launch<C, O>::kBlocksPerCu;
-        if (blocks > cap) blocks = cap;
+        constexpr int kMax = kMaxTilesPerWave<C, O>;
+        if (blocks > cap && (kMax == 0 || tiles <= static_cast<int64_t>(kMax) * cap * kWaves)) blocks = cap;
     }
     return static_cast<unsigned>(blocks);
 }

@@ -216,12 +216,13 @@ def test_gather_out_of_range_entries_are_zero_rows(dev, C):
     assert not bits(ng[bad]).any()
 
 
-@pytest.mark.parametrize("C", [192, 384, 768])
-def test_gathers_loop_over_tiles_with_a_ragged_tail(dev, C):
-    # 49,157 output rows: more than two passes of the capped C = 384 grids
-    # (4 workgroups per CU x 4 waves x 4 rows for the plain gather, 3 x 4 x 8
-    # for norm_gather on 256 CUs), ending in a part-filled tile.
-    n_src, n_out = 20000, 49157
+@pytest.mark.parametrize("C,n_out", [(192, 45061), (384, 45061), (384, 140005), (768, 45061)])
+def test_gathers_loop_over_tiles_with_a_ragged_tail(dev, C, n_out):
+    # 45,061 output rows: 1.8 and 2.75 tiles per wave in the capped C = 384 grids
+    # (12 one-wave workgroups per CU x 8 rows for norm_gather, 4 x 4 waves x 4
+    # rows for the plain gather, on 256 CUs), ending in a part-filled tile.
+    # 140,005 rows: past both entries' limits, one tile per wave.
+    n_src = 20000
     x = workloads.normal_rows(71, n_src, C, mean=0.2, std=1.7)
     table = workloads.table_with_bad_entries(72, n_out, n_src)
     tx, tt = to_dev(x, dev), to_dev(table, dev)

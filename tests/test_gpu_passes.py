@@ -1,11 +1,14 @@
-"""Every row kernel at a row count where each wave of the capped C = 384
-grids takes several row tiles and the last tile is only part filled, with
-every output element compared against the oracle.
+"""Every row kernel at row counts that exercise both launch shapes of the C = 384
+kernels, with every output element compared against the oracle.
 
-73,733 rows is three passes of the widest capped C = 384 grid (ln_fixed:
-3 workgroups per compute unit x 4 waves x 8 rows on 256 CUs = 24,576 rows a
-pass) plus 5 rows; at C = 192 and 768 the grids hold one tile per wave, and
-the same count ends in a part-filled tile there too.
+* 45,061 rows: each wave of the capped C = 384 grids takes 1.5-2.8 row tiles
+  (ln_fixed: 3 workgroups per compute unit x 4 waves on 256 CUs = 3,072 waves
+  for 5,633 tiles of 8 rows; add_ln: 2,048 waves), within every entry's limit of
+  tiles per wave, and the last tile is part filled (45,061 = 8 x 5,632 + 5).
+* 140,005 rows (C = 384 only): past every entry's limit, so the same kernels
+  run one tile per wave.
+At C = 192 and 768 the grids hold one tile per wave (C = 768 ln_fixed is
+capped and loops) and the same counts end in part-filled tiles.
 """
 import numpy as np
 import pytest
@@ -20,15 +23,15 @@ lwg = pytest.importorskip("layernorm_window_gather_amd")
 
 pytestmark = pytest.mark.gpu
 
-ROWS = 73733
+CASES = [(192, 45061), (384, 45061), (384, 140005), (768, 45061)]
 
 
-@pytest.fixture(scope="module", params=[192, 384, 768])
+@pytest.fixture(scope="module", params=CASES, ids=lambda c: f"C{c[0]}-rows{c[1]}")
 def rows_case(request):
-    C = request.param
-    nc, off = workloads.stress_row_classes(90 + C, ROWS)
-    res = workloads.mixed_rows(91 + C, ROWS, C, nc, off)
-    br = workloads.mixed_rows(92 + C, ROWS, C, nc, off, offset_mean=0.0)
+    C, rows = request.param
+    nc, off = workloads.stress_row_classes(90 + C, rows)
+    res = workloads.mixed_rows(91 + C, rows, C, nc, off)
+    br = workloads.mixed_rows(92 + C, rows, C, nc, off, offset_mean=0.0)
     gamma = workloads.normal_rows(93 + C, 1, C)[0]
     beta = workloads.normal_rows(94 + C, 1, C, std=0.1)[0]
     return C, br, res, gamma, beta
@@ -36,7 +39,7 @@ def rows_case(request):
 
 def test_ln_and_add_ln(dev, rows_case):
     C, br, res, _, _ = rows_case
-    print(f"[passes] ln_fixed / add_ln C={C} rows={ROWS}", flush=True)
+    print(f"[passes] ln_fixed / add_ln C={C} rows={len(res)}", flush=True)
     assert_ln_close(host(lwg.ln_fixed(to_dev(res, dev))), oracle.layer_norm(res), f"ln_fixed C={C}")
     r, y = lwg.add_ln(to_dev(br, dev), to_dev(res, dev))
     r_ref, y_ref = oracle.add_ln(br, res)
@@ -46,7 +49,7 @@ def test_ln_and_add_ln(dev, rows_case):
 
 def test_affine(dev, rows_case):
     C, br, res, gamma, beta = rows_case
-    print(f"[passes] ln_affine / add_ln_affine C={C} rows={ROWS}", flush=True)
+    print(f"[passes] ln_affine / add_ln_affine C={C} rows={len(res)}", flush=True)
     tg, tb = to_dev(gamma, dev), to_dev(beta, dev)
     assert_ln_close(host(lwg.ln_affine(to_dev(res, dev), tg, tb)),
                     oracle.layer_norm_affine(res, gamma, beta), f"ln_affine C={C}")
@@ -60,10 +63,11 @@ def test_reverse_add_ln_with_a_permutation(dev, rows_case):
     # the inverse table here is a seeded permutation of more window rows than
     # tokens, so the branch of token i is rows[inverse[i]]
     C, br, res, _, _ = rows_case
-    print(f"[passes] window_reverse_add_ln C={C} rows={ROWS}", flush=True)
-    n_win = ROWS + 1000
+    print(f"[passes] window_reverse_add_ln C={C} rows={len(res)}", flush=True)
+    n = len(res)
+    n_win = n + 1000
     rows = workloads.normal_rows(95 + C, n_win, C)
-    inverse = np.random.default_rng(96 + C).permutation(n_win)[:ROWS].astype(np.int32)
+    inverse = np.random.default_rng(96 + C).permutation(n_win)[:n].astype(np.int32)
     r, y = lwg.window_reverse_add_ln(to_dev(rows, dev), to_dev(inverse, dev), to_dev(res, dev))
     r_ref, y_ref = oracle.add_ln(oracle.window_gather(rows, inverse), res)
     assert_bit_exact(host(r), r_ref, f"window_reverse_add_ln residual C={C}")
@@ -73,9 +77,9 @@ def test_reverse_add_ln_with_a_permutation(dev, rows_case):
 def test_add_norm_gather_with_padding(dev, rows_case):
     # every token once, in a seeded order, with -1 padding entries mixed in
     C, br, res, _, _ = rows_case
-    print(f"[passes] add_norm_gather C={C} rows={ROWS}", flush=True)
+    print(f"[passes] add_norm_gather C={C} rows={len(res)}", flush=True)
     rng = np.random.default_rng(97 + C)
-    table = np.concatenate([np.arange(ROWS), np.full(4099, -1)])
+    table = np.concatenate([np.arange(len(res)), np.full(4099, -1)])
     table = table[rng.permutation(table.size)].astype(np.int32)
     r, g = lwg.add_norm_gather(to_dev(br, dev), to_dev(res, dev), to_dev(table, dev))
     r_ref, g_ref = oracle.add_norm_gather(br, res, table)
