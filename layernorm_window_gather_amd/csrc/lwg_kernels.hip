@@ -875,8 +875,8 @@ template <> struct Launch<768, Op::kLnAffine> : Tuned<0, false, 1> {};
 // for norm_gather (-4.4%) and add_norm_gather (-6.0%) at 2.9 and 2.2 tiles per
 // wave, and for add_ln, window_reverse_add_ln and add_ln_affine (-3 to -7%) at
 // 4 tiles per wave, but slower for ln_fixed (+2.0%, 2.7 tiles per wave) and
-// the plain gather (+1.2%, 4.4 tiles per wave). C = 768 was only measured at
-// its workload size and keeps its cap.
+// the plain gather (+1.2%, 4.4 tiles per wave). C = 768 ln_fixed on 131,040
+// rows: -10.4% with the same limit of 3 (its 32,760-row size keeps the cap).
 template <int C, Op O> constexpr int kMaxTilesPerWave = 0;
 template <> constexpr int kMaxTilesPerWave<384, Op::kLn> = 3;
 template <> constexpr int kMaxTilesPerWave<384, Op::kAddLn> = 3;
@@ -886,6 +886,7 @@ template <> constexpr int kMaxTilesPerWave<384, Op::kLnAffine> = 3;
 template <> constexpr int kMaxTilesPerWave<384, Op::kNormGather> = 2;
 template <> constexpr int kMaxTilesPerWave<384, Op::kAddNormGather> = 2;
 template <> constexpr int kMaxTilesPerWave<384, Op::kGather> = 5;
+template <> constexpr int kMaxTilesPerWave<768, Op::kLn> = 3;
 
 
 // Compute units of the device, queried on first use (0 = not yet known). Only

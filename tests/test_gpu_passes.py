@@ -7,8 +7,10 @@ kernels, with every output element compared against the oracle.
   tiles per wave, and the last tile is part filled (45,061 = 8 x 5,632 + 5).
 * 140,005 rows (C = 384 only): past every entry's limit, so the same kernels
   run one tile per wave.
-At C = 192 and 768 the grids hold one tile per wave (C = 768 ln_fixed is
-capped and loops) and the same counts end in part-filled tiles.
+At C = 192 and 768 the grids at 45,061 rows hold one tile per wave (C = 768
+ln_fixed is past its limit there; it runs capped, with waves looping, at the
+32,760-row patch-merge size in tests/test_gpu_widths_affine.py), and the same
+counts end in part-filled tiles.
 """
 import numpy as np
 import pytest
