@@ -806,6 +806,8 @@ using Streaming = Hints<true, true>;
 //  * C = 192, one tile per wave: the pipelined form of ln_fixed, add_ln and the
 //    fused residual kernels issues the tile's loads ahead of the loop test and
 //    measured 2-4% faster; the gathers and ln_affine are fastest as they are.
+//    (ln_fixed and add_ln carry caps that apply only to smaller inputs; see
+//    kMaxTilesPerWave below.)
 //  * kPriority: the pipelined two-input kernels at C = 384 and ln_affine at
 //    C = 192 issue their loads at wave priority 1 (s_setprio) and drop to 0
 //    for the arithmetic: C = 384 add_ln -7%, add_ln_affine -5%,
@@ -848,8 +850,8 @@ template <int Cap, bool Prefetch, int Priority = 0, int Chunks = 0, int Waves = 
 template <int C, Op O> constexpr int kChunksOf = Launch<C, O>::kChunks > 0 ? Launch<C, O>::kChunks : Width<C>::K;
 template <int C, Op O>
 constexpr bool kChunksOk = O == Op::kGather || kChunksOf<C, O> == Width<C>::K;
-template <> struct Launch<192, Op::kLn> : Tuned<0, true> {};
-template <> struct Launch<192, Op::kAddLn> : Tuned<0, true> {};
+template <> struct Launch<192, Op::kLn> : Tuned<4, true> {};
+template <> struct Launch<192, Op::kAddLn> : Tuned<3, true> {};
 template <> struct Launch<192, Op::kReverseAddLn> : Tuned<0, true> {};
 template <> struct Launch<192, Op::kAddNormGather> : Tuned<0, true> {};
 template <> struct Launch<192, Op::kAddLnAffine> : Tuned<0, true> {};
@@ -877,6 +879,10 @@ template <> struct Launch<768, Op::kLnAffine> : Tuned<0, false, 1> {};
 // 4 tiles per wave, but slower for ln_fixed (+2.0%, 2.7 tiles per wave) and
 // the plain gather (+1.2%, 4.4 tiles per wave). C = 768 ln_fixed on 131,040
 // rows: -10.4% with the same limit of 3 (its 32,760-row size keeps the cap).
+// The same rule gives C = 192 ln_fixed and add_ln a cap (4 and 3 workgroups
+// per compute unit) for inputs where their waves take at most 2 tiles: -13%
+// (add_ln, 32,760 rows), -10% (ln_fixed, 48,960 rows), -4% (ln_fixed, 65,520
+// rows); at the model's 131,040 rows they run one tile per wave as before.
 template <int C, Op O> constexpr int kMaxTilesPerWave = 0;
 template <> constexpr int kMaxTilesPerWave<384, Op::kLn> = 3;
 template <> constexpr int kMaxTilesPerWave<384, Op::kAddLn> = 3;
@@ -887,6 +893,8 @@ template <> constexpr int kMaxTilesPerWave<384, Op::kNormGather> = 2;
 template <> constexpr int kMaxTilesPerWave<384, Op::kAddNormGather> = 2;
 template <> constexpr int kMaxTilesPerWave<384, Op::kGather> = 5;
 template <> constexpr int kMaxTilesPerWave<768, Op::kLn> = 3;
+template <> constexpr int kMaxTilesPerWave<192, Op::kLn> = 2;
+template <> constexpr int kMaxTilesPerWave<192, Op::kAddLn> = 2;
 
 
 // Compute units of the device, queried on first use (0 = not yet known). Only
