@@ -852,9 +852,9 @@ template <int C, Op O>
 constexpr bool kChunksOk = O == Op::kGather || kChunksOf<C, O> == Width<C>::K;
 template <> struct Launch<192, Op::kLn> : Tuned<4, true> {};
 template <> struct Launch<192, Op::kAddLn> : Tuned<3, true> {};
-template <> struct Launch<192, Op::kReverseAddLn> : Tuned<0, true> {};
+template <> struct Launch<192, Op::kReverseAddLn> : Tuned<3, true> {};
 template <> struct Launch<192, Op::kAddNormGather> : Tuned<0, true> {};
-template <> struct Launch<192, Op::kAddLnAffine> : Tuned<0, true> {};
+template <> struct Launch<192, Op::kAddLnAffine> : Tuned<2, true> {};
 template <> struct Launch<384, Op::kLn> : Tuned<3, true> {};
 template <> struct Launch<384, Op::kNormGather> : Tuned<12, true, 0, 0, 1> {};
 template <> struct Launch<384, Op::kGather> : Tuned<4, false, 0, 3> {};
@@ -879,10 +879,13 @@ template <> struct Launch<768, Op::kLnAffine> : Tuned<0, false, 1> {};
 // 4 tiles per wave, but slower for ln_fixed (+2.0%, 2.7 tiles per wave) and
 // the plain gather (+1.2%, 4.4 tiles per wave). C = 768 ln_fixed on 131,040
 // rows: -10.4% with the same limit of 3 (its 32,760-row size keeps the cap).
-// The same rule gives C = 192 ln_fixed and add_ln a cap (4 and 3 workgroups
-// per compute unit) for inputs where their waves take at most 2 tiles: -13%
-// (add_ln, 32,760 rows), -10% (ln_fixed, 48,960 rows), -4% (ln_fixed, 65,520
-// rows); at the model's 131,040 rows they run one tile per wave as before.
+// The same rule gives C = 192 ln_fixed, add_ln, window_reverse_add_ln and
+// add_ln_affine a cap (4, 3, 3 and 2 workgroups per compute unit) for inputs
+// where their waves take at most 2 tiles: -13% (add_ln), -10%
+// (window_reverse_add_ln, add_ln_affine) at 32,760 rows, -10% and -4%
+// (ln_fixed) at 48,960 and 65,520 rows; at the model's 131,040 rows they run
+// one tile per wave as before. The C = 192 gathers, add_norm_gather and
+// ln_affine gained at most 2% or lost with caps at those sizes.
 template <int C, Op O> constexpr int kMaxTilesPerWave = 0;
 template <> constexpr int kMaxTilesPerWave<384, Op::kLn> = 3;
 template <> constexpr int kMaxTilesPerWave<384, Op::kAddLn> = 3;
@@ -895,6 +898,8 @@ template <> constexpr int kMaxTilesPerWave<384, Op::kGather> = 5;
 template <> constexpr int kMaxTilesPerWave<768, Op::kLn> = 3;
 template <> constexpr int kMaxTilesPerWave<192, Op::kLn> = 2;
 template <> constexpr int kMaxTilesPerWave<192, Op::kAddLn> = 2;
+template <> constexpr int kMaxTilesPerWave<192, Op::kReverseAddLn> = 2;
+template <> constexpr int kMaxTilesPerWave<192, Op::kAddLnAffine> = 2;
 
 
 // Compute units of the device, queried on first use (0 = not yet known). Only
