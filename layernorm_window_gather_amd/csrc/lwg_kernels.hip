@@ -792,8 +792,9 @@ using Streaming = Hints<true, true>;
 // Per (width, op): kBlocksPerCu caps the grid at that many workgroups per
 // compute unit (0 = one tile per wave); kPrefetch selects the software-pipelined
 // row loop (the next tile's loads issued before the current tile is
-// normalised). Each entry was measured against the alternatives on cold
-// buffers, in interleaved runs on one MI355X:
+// normalised); kPriority, kChunks and kWaves are described below. Each entry
+// was measured against the alternatives on cold buffers, in interleaved runs on
+// one MI355X:
 //  * C = 384: with a cap each wave takes 1.3-2.3 tiles and, pipelined,
 //    normalises one while the next loads: ln_fixed -11%, norm_gather -10%,
 //    add_ln -4%, window_reverse_add_ln -4%, add_ln_affine -6%; ln_affine gains
@@ -806,8 +807,9 @@ using Streaming = Hints<true, true>;
 //  * C = 192, one tile per wave: the pipelined form of ln_fixed, add_ln and the
 //    fused residual kernels issues the tile's loads ahead of the loop test and
 //    measured 2-4% faster; the gathers and ln_affine are fastest as they are.
-//    (ln_fixed and add_ln carry caps that apply only to smaller inputs; see
-//    kMaxTilesPerWave below.)
+//    (ln_fixed, add_ln, window_reverse_add_ln and add_ln_affine carry caps
+//    that apply only to inputs smaller than the model's; see kMaxTilesPerWave
+//    below.)
 //  * kPriority: the pipelined two-input kernels at C = 384 and ln_affine at
 //    C = 192 issue their loads at wave priority 1 (s_setprio) and drop to 0
 //    for the arithmetic: C = 384 add_ln -7%, add_ln_affine -5%,
@@ -850,11 +852,13 @@ template <int Cap, bool Prefetch, int Priority = 0, int Chunks = 0, int Waves = 
 template <int C, Op O> constexpr int kChunksOf = Launch<C, O>::kChunks > 0 ? Launch<C, O>::kChunks : Width<C>::K;
 template <int C, Op O>
 constexpr bool kChunksOk = O == Op::kGather || kChunksOf<C, O> == Width<C>::K;
+//                                                  Tuned<cap, pipelined, priority, chunks, waves per workgroup>
 template <> struct Launch<192, Op::kLn> : Tuned<4, true> {};
 template <> struct Launch<192, Op::kAddLn> : Tuned<3, true> {};
 template <> struct Launch<192, Op::kReverseAddLn> : Tuned<3, true> {};
 template <> struct Launch<192, Op::kAddNormGather> : Tuned<0, true> {};
 template <> struct Launch<192, Op::kAddLnAffine> : Tuned<2, true> {};
+template <> struct Launch<192, Op::kLnAffine> : Tuned<0, false, 1> {};
 template <> struct Launch<384, Op::kLn> : Tuned<3, true> {};
 template <> struct Launch<384, Op::kNormGather> : Tuned<12, true, 0, 0, 1> {};
 template <> struct Launch<384, Op::kGather> : Tuned<4, false, 0, 3> {};
@@ -862,7 +866,6 @@ template <> struct Launch<384, Op::kAddLn> : Tuned<2, true, 1> {};
 template <> struct Launch<384, Op::kReverseAddLn> : Tuned<2, true, 1> {};
 template <> struct Launch<384, Op::kAddLnAffine> : Tuned<2, true, 1> {};
 template <> struct Launch<384, Op::kLnAffine> : Tuned<3, false> {};
-template <> struct Launch<192, Op::kLnAffine> : Tuned<0, false, 1> {};
 template <> struct Launch<384, Op::kAddNormGather> : Tuned<4, true> {};
 template <> struct Launch<768, Op::kLn> : Tuned<3, true> {};
 template <> struct Launch<768, Op::kLnAffine> : Tuned<0, false, 1> {};
