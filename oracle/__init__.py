@@ -1,9 +1,10 @@
 """CPU oracle for the fixed-width LayerNorm / shifted-window gather row pipeline.
 
-TEST INFRASTRUCTURE. Only the tests, ``__graft_entry__.smoke()`` and the
-``cpu_baseline`` leg of ``bench.py`` import this package. The product path (the
-HIP library under ``include/lwg.h`` and its Python binding) never imports,
-calls or links anything here, and this package imports nothing from it.
+TEST INFRASTRUCTURE. Only the tests, ``__graft_entry__.smoke()`` and two legs
+of ``bench.py`` (the sampled parity gate that runs before any timing, and the
+``cpu_baseline`` timing) import this package. The product path (the HIP
+library under ``include/lwg.h`` and its Python binding) never imports, calls
+or links anything here, and this package imports nothing from it.
 
 Everything is plain numpy in float64, written from the definitions on the page
 "Pangu-Weather inference optimisation on Hygon BW1000 (gfx936)"
