@@ -289,3 +289,21 @@ def test_huge_grids_are_refused_without_overflow():
     assert st == _lib.LWG_ERR_INVALID_ARGUMENT
     st = lib.lwg_window_inverse_build(big, big, big, 2, 6, 12, 0, 0, 0, ctypes.c_void_p(0x1000), 1, None)
     assert st == _lib.LWG_ERR_INVALID_ARGUMENT
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    # With no liblwg.so there is no fallback: loading the library raises and
+    # names the build command. Run in a fresh process so the already-loaded
+    # library of this one is not reused.
+    import subprocess
+    import sys
+    code = ("import layernorm_window_gather_amd as lwg\n"
+            "try:\n"
+            "    lwg.library()\n"
+            "except RuntimeError as e:\n"
+            "    print('RAISED', e)\n")
+    env = dict(os.environ, LWG_LIBRARY=str(tmp_path / "absent" / "liblwg.so"))
+    run = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True, text=True,
+                         timeout=300)
+    assert run.returncode == 0, run.stderr
+    assert "RAISED" in run.stdout and "no fallback" in run.stdout, run.stdout + run.stderr
