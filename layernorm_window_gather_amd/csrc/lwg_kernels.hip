@@ -499,10 +499,13 @@ __global__ __launch_bounds__(kBlock) void add_ln_affine_kernel(const chunk_t* br
 // Output-major gather: lane group j reads table[j] and, for a valid entry,
 // the whole source row; padding and out-of-range entries read nothing and
 // store +0.0 (LayerNorm of a zero row is exactly +0.0 as well).
-template <int C, int K, class H>
+// With kPrio > 0 the table read and the row loads are issued at that wave
+// priority, as in load_tile.
+template <int C, int K, class H, int kPrio = 0>
 __device__ __forceinline__ void load_gathered(const chunk_t* x, int64_t n_src, const int32_t* table,
                                               int64_t n_out, int64_t w, int lane, chunk_t (&v)[K]) {
     using T = Tile<C, K>;
+    if constexpr (kPrio > 0) __builtin_amdgcn_s_setprio(kPrio);
     const int64_t j = w * T::kRowsPerWave + lane / T::kLanes;
     const int32_t t = j < n_out ? table[j] : -1;
     zero(v);
@@ -511,9 +514,10 @@ __device__ __forceinline__ void load_gathered(const chunk_t* x, int64_t n_src, c
 #pragma unroll
         for (int k = 0; k < K; ++k) v[k] = load16<H>(x + src + k * T::kLanes);
     }
+    if constexpr (kPrio > 0) __builtin_amdgcn_s_setprio(0);
 }
 
-template <int C, int K, bool kNorm, class H, bool kPrefetch, int kWaves>
+template <int C, int K, bool kNorm, class H, bool kPrefetch, int kWaves, int kPrio>
 __global__ __launch_bounds__(64 * kWaves) void gather_kernel(const chunk_t* __restrict__ x, int64_t n_src,
                                                              const int32_t* __restrict__ table,
                                                              int64_t n_out, chunk_t* __restrict__ out,
@@ -524,10 +528,10 @@ __global__ __launch_bounds__(64 * kWaves) void gather_kernel(const chunk_t* __re
         const int64_t stride = wave_stride_in<kWaves>();
         int64_t w = first_wave_in<kWaves>();
         chunk_t v[K];
-        load_gathered<C, K, H>(x, n_src, table, n_out, w, lane, v);
+        load_gathered<C, K, H, kPrio>(x, n_src, table, n_out, w, lane, v);
         for (; w * T::kRowsPerWave < n_out; w += stride) {
             chunk_t next[K];
-            load_gathered<C, K, H>(x, n_src, table, n_out, w + stride, lane, next);
+            load_gathered<C, K, H, kPrio>(x, n_src, table, n_out, w + stride, lane, next);
             if constexpr (kNorm) layer_norm_lane<C, K>(v, eps);
             store_tile<C, K, H>(out, w, n_out, lane, v);
 #pragma unroll
@@ -538,6 +542,7 @@ __global__ __launch_bounds__(64 * kWaves) void gather_kernel(const chunk_t* __re
         for (int64_t w = first_wave_in<kWaves>(); w * T::kRowsPerWave < n_out; w += wave_stride_in<kWaves>()) {
             const int64_t j = w * T::kRowsPerWave + lane / T::kLanes;
             const bool live = j < n_out;
+            if constexpr (kPrio > 0) __builtin_amdgcn_s_setprio(kPrio);
             const int32_t t = live ? table[j] : -1;
             const bool valid = t >= 0 && static_cast<int64_t>(t) < n_src;
             const int64_t src = static_cast<int64_t>(t) * T::kChunks + sub;
@@ -547,6 +552,7 @@ __global__ __launch_bounds__(64 * kWaves) void gather_kernel(const chunk_t* __re
 #pragma unroll
                 for (int k = 0; k < K; ++k) v[k] = load16<H>(x + src + k * T::kLanes);
             }
+            if constexpr (kPrio > 0) __builtin_amdgcn_s_setprio(0);
             if constexpr (kNorm) layer_norm_lane<C, K>(v, eps);
             if (live) {
                 const int64_t dst = j * T::kChunks + sub;
@@ -814,7 +820,9 @@ using Streaming = Hints<true, true>;
 //    C = 192 issue their loads at wave priority 1 (s_setprio) and drop to 0
 //    for the arithmetic: C = 384 add_ln -7%, add_ln_affine -5%,
 //    window_reverse_add_ln -1%, C = 192 ln_affine -2.5%. On the one-tile-per-
-//    wave kernels it cost up to 4% and is off.
+//    wave kernels it cost up to 4% and is off. The C = 384 norm_gather took it
+//    once it ran one-wave workgroups (-2.5 to -2.8%; with four-wave workgroups
+//    it had been neutral).
 //  * C = 384 norm_gather runs one wave per workgroup, 12 workgroups per
 //    compute unit (the same 12 waves as 3 four-wave workgroups): -1.9%. Caps
 //    of 8, 16 and 24 one-wave workgroups, the loop without the pipeline, and
@@ -860,7 +868,7 @@ template <> struct Launch<192, Op::kAddNormGather> : Tuned<0, true> {};
 template <> struct Launch<192, Op::kAddLnAffine> : Tuned<2, true> {};
 template <> struct Launch<192, Op::kLnAffine> : Tuned<0, false, 1> {};
 template <> struct Launch<384, Op::kLn> : Tuned<3, true> {};
-template <> struct Launch<384, Op::kNormGather> : Tuned<12, true, 0, 0, 1> {};
+template <> struct Launch<384, Op::kNormGather> : Tuned<12, true, 1, 0, 1> {};
 template <> struct Launch<384, Op::kGather> : Tuned<4, false, 0, 3> {};
 template <> struct Launch<384, Op::kAddLn> : Tuned<2, true, 1> {};
 template <> struct Launch<384, Op::kReverseAddLn> : Tuned<2, true, 1> {};
@@ -964,7 +972,7 @@ hipError_t gather_c(const void* x, int64_t n_src, const int32_t* table, int64_t 
                     void* out, hipStream_t s) {
     constexpr Op O = kNorm ? Op::kNormGather : Op::kGather;
     using L = Launch<C, O>;
-    gather_kernel<C, kChunksOf<C, O>, kNorm, typename L::H, L::kPrefetch, L::kWaves>
+    gather_kernel<C, kChunksOf<C, O>, kNorm, typename L::H, L::kPrefetch, L::kWaves, L::kPriority>
         <<<grid_for<C, O>(n_out), 64 * L::kWaves, 0, s>>>(
         static_cast<const chunk_t*>(x), n_src, table, n_out, static_cast<chunk_t*>(out), eps);
     return hipGetLastError();
