@@ -224,3 +224,22 @@ def test_affine_output_at_the_binary16_overflow_threshold(dev, C):
     assert_bit_exact(host(lwg.ln_affine(xd, tg, tb, eps)), ref, f"ln_affine C={C} at the overflow threshold")
     r, y = lwg.add_ln_affine(xd, torch.zeros_like(xd), tg, tb, eps)
     assert_bit_exact(host(y), ref, f"add_ln_affine C={C} at the overflow threshold")
+
+
+@pytest.mark.parametrize("eps", [5e-324, 1e-310, 1e-300])
+def test_subnormal_and_tiny_eps(dev, eps):
+    """eps may be any finite positive binary64, down to the smallest subnormal.
+    A constant row then has var + eps = eps, and its rsqrt must not flush to
+    infinity (0 * inf would give NaN): the outputs stay +0.0, as in the oracle.
+    Rows with a spread are unaffected by so small an eps."""
+    C = 384
+    rows = np.stack([np.full(C, 3.5), np.array([1.0, -1.0] * (C // 2)), np.zeros(C)] +
+                    [workloads.normal_rows(900 + i, 1, C)[0].astype(np.float64) for i in range(5)]).astype(np.float16)
+    ref = oracle.layer_norm(rows, eps)
+    assert not np.isnan(ref).any() and not bits(ref[[0, 2]]).any()
+    xd = to_dev(rows, dev)
+    assert_bit_exact(host(lwg.ln_fixed(xd, eps)), ref, f"ln_fixed eps={eps}")
+    zeros = torch.zeros_like(xd)
+    assert_bit_exact(host(lwg.add_ln(xd, zeros, eps)[1]), ref, f"add_ln eps={eps}")
+    ident = torch.arange(rows.shape[0], dtype=torch.int32, device=dev)
+    assert_bit_exact(host(lwg.norm_gather(xd, ident, eps)), ref, f"norm_gather eps={eps}")
