@@ -804,7 +804,9 @@ using Streaming = Hints<true, true>;
 //  * C = 384: with a cap each wave takes 1.3-2.3 tiles and, pipelined,
 //    normalises one while the next loads: ln_fixed -11%, norm_gather -10%,
 //    add_ln -4%, window_reverse_add_ln -4%, add_ln_affine -6%; ln_affine gains
-//    9% from the cap alone (it loses with the pipeline). The single-input
+//    from the cap alone (it loses with the pipeline): cap 3 at first (-9%),
+//    cap 4 since its parameters are widened in LDS (126 VGPRs, 4 waves per
+//    SIMD; -4% against cap 3, and cap 4 with priority -3%). The single-input
 //    pipelined kernels hold 136-140 VGPRs (3 waves per SIMD) and take cap 3.
 //    The two-input ones hold 168-180 and take cap 2: caps 3 and 4 measured
 //    3-16% slower, although 3 waves of 168 VGPRs would fit. add_norm_gather
@@ -873,7 +875,7 @@ template <> struct Launch<384, Op::kGather> : Tuned<4, false, 0, 3> {};
 template <> struct Launch<384, Op::kAddLn> : Tuned<2, true, 1> {};
 template <> struct Launch<384, Op::kReverseAddLn> : Tuned<2, true, 1> {};
 template <> struct Launch<384, Op::kAddLnAffine> : Tuned<2, true, 1> {};
-template <> struct Launch<384, Op::kLnAffine> : Tuned<3, false> {};
+template <> struct Launch<384, Op::kLnAffine> : Tuned<4, false> {};
 template <> struct Launch<384, Op::kAddNormGather> : Tuned<4, true> {};
 template <> struct Launch<768, Op::kLn> : Tuned<3, true> {};
 template <> struct Launch<768, Op::kLnAffine> : Tuned<0, false, 1> {};
