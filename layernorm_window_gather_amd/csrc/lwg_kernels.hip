@@ -165,8 +165,9 @@ __device__ __forceinline__ void residual_add(const chunk_t (&branch)[K], chunk_t
 }
 
 // 1/sqrt(a) for a > 0: the hardware reciprocal-square-root estimate refined by
-// one Newton step, r' = r (3/2 - a r^2 / 2), which roughly squares its relative
-// error and lands within a few ulp of the binary64 result. Inf and NaN give NaN.
+// one Newton step, r' = r (3/2 - a r^2 / 2), which takes a relative error e to
+// about 1.5 e^2: from the estimate's ~2^-24 to ~2^-47, far below the 2^-11 of a
+// binary16 result. Inf and NaN give NaN.
 __device__ __forceinline__ double rsqrt_refined(double a) {
     const double r = __builtin_amdgcn_rsq(a);
     const double h = 0.5 * a * r;
@@ -771,8 +772,9 @@ __global__ __launch_bounds__(kBlock) void bias_gelu_kernel(const f32x4_t* x, con
 // K (chunks per lane) is fixed per width, so that every LayerNorm kernel of one
 // width reduces a row in the same order and their outputs agree bit for bit:
 // K = 3 at C = 192 and K = 6 at C = 384, i.e. 8 lanes per row, each wave
-// instruction reading whole 128-byte lines of 8 rows; K = 6 at C = 768. (4 lanes per row, 64-byte
-// pieces of a line per instruction, measured 10-20% slower.)
+// instruction reading whole 128-byte lines of 8 rows (4 lanes per row, 64-byte
+// pieces of a line per instruction, measured 10-20% slower); K = 6 at C = 768,
+// 16 lanes per row, 256 contiguous bytes of each of 4 rows per instruction.
 // Every kernel streams its inputs once and never re-reads its outputs, so all
 // loads and stores carry the non-temporal hint; on cold data that beat plain
 // and store-only-hinted accesses for every kernel. The grid is one tile per
@@ -805,13 +807,18 @@ using Streaming = Hints<true, true>;
 //    normalises one while the next loads: ln_fixed -11%, norm_gather -10%,
 //    add_ln -4%, window_reverse_add_ln -4%, add_ln_affine -6%; ln_affine gains
 //    from the cap alone (it loses with the pipeline): cap 3 at first (-9%),
-//    cap 4 since its parameters are widened in LDS (126 VGPRs, 4 waves per
-//    SIMD; -4% against cap 3, and cap 4 with priority -3%). The single-input
-//    pipelined kernels hold 136-140 VGPRs (3 waves per SIMD) and take cap 3.
-//    The two-input ones hold 168-180 and take cap 2: caps 3 and 4 measured
-//    3-16% slower, although 3 waves of 168 VGPRs would fit. add_norm_gather
-//    (117 VGPRs) is fastest pipelined at cap 4: -3.4% against cap 2 without
-//    the pipeline.
+//    cap 4 since its parameters are widened in LDS (128 VGPRs, 4 waves per
+//    SIMD; -4% against cap 3, and cap 4 with priority -3%). Register counts
+//    (the compiler's NumVgprs) set how many waves are resident, and these caps
+//    fill exactly that: the single-input pipelined kernels hold 150-156 VGPRs
+//    (3 waves per SIMD) and take cap 3; add_ln, window_reverse_add_ln and
+//    add_ln_affine hold 180-194 (2 waves per SIMD) and take cap 2, caps 3 and
+//    4 (a second generation of workgroups) measuring 3-16% slower.
+//    add_norm_gather (188 VGPRs) is the exception: fastest pipelined at cap 4,
+//    -3.4% against cap 2 without the pipeline. Halving the registers (each
+//    pass re-widening the binary16 values instead of keeping the binary64
+//    deviations) raised residency and made every LayerNorm kernel slower,
+//    +3-7% at C = 192 and +13-23% at C = 384, with or without larger caps.
 //  * C = 192, one tile per wave: the pipelined form of ln_fixed, add_ln and the
 //    fused residual kernels issues the tile's loads ahead of the loop test and
 //    measured 2-4% faster; the gathers and ln_affine are fastest as they are.
@@ -835,7 +842,7 @@ using Streaming = Hints<true, true>;
 //    instruction) capped at 4 workgroups per compute unit: -2 to -3% against
 //    K = 6 at one tile per wave; caps 2, 3, 5 and 8 and the pipelined loop
 //    measured equal or worse.
-//  * C = 768: ln_fixed (109 VGPRs) pipelined at cap 3, -3.4 to -4.5% (cap 2
+//  * C = 768: ln_fixed (150 VGPRs) pipelined at cap 3, -3.4 to -4.5% (cap 2
 //    +1%, cap 4 +10%, uncapped -2%); ln_affine at one tile per wave with load
 //    priority, -1.1 to -1.4% (caps 2-4 +3 to +10%).
 //  * Everything else: the default.
@@ -948,6 +955,12 @@ unsigned grid_for(int64_t rows) {
         constexpr int kMax = kMaxTilesPerWave<C, O>;
         if (blocks > cap && (kMax == 0 || tiles <= static_cast<int64_t>(kMax) * cap * kWaves)) blocks = cap;
     }
+    // A dispatch counts its work-items in 32 bits: past 2^32 of them (C = 192
+    // ln_fixed on more than 2^29 rows) the grid stops at the largest size below
+    // that, and the waves loop over the remaining tiles with the grid stride,
+    // as on a capped grid.
+    constexpr int64_t kMaxBlocks = ((int64_t{1} << 32) - 1) / (64 * kWaves);
+    if (blocks > kMaxBlocks) blocks = kMaxBlocks;
     return static_cast<unsigned>(blocks);
 }
 

@@ -156,3 +156,37 @@ def test_large_add_norm_gather(dev, big):
     ref = np.zeros((js.size, lv.channels), np.float16)
     ref[ok] = oracle.layer_norm(oracle.residual_sum(x[t[ok]], branch[t[ok]]))
     assert_ln_close(take(out, js), ref, "large add_norm_gather out, sampled rows")
+
+
+def test_grid_past_2_to_32_work_items(dev):
+    """In-place ln_fixed at C = 192 on 2**29 + 1000 rows (192 GiB). One tile per
+    wave would take more than 2**32 work-items, which one dispatch cannot count,
+    so the launch clamps the grid and the waves loop over the rest. The input
+    repeats a seeded block of rows; the rows just below and above 2**29 (the
+    last ones the clamped grid's first pass reaches, and the ones only the loop
+    reaches), the first and last rows and seeded random rows must all be
+    normalised."""
+    C, B = 192, 4096
+    n = (1 << 29) + 1000
+    need = n * C * 2
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    free, _ = torch.cuda.mem_get_info(dev)
+    if free < need + (4 << 30):
+        pytest.skip(f"needs {need / 2**30:.0f} GiB of free device memory; {free / 2**30:.0f} GiB free")
+    print(f"[large] in-place ln_fixed, {n} rows x {C}", flush=True)
+    block = workloads.normal_rows(110, B, C)
+    tb = to_dev(block, dev)
+    x = torch.empty(n, C, dtype=torch.float16, device=dev)
+    q = n // B
+    x[: q * B].view(q, B, C).copy_(tb.unsqueeze(0).expand(q, B, C))
+    x[q * B:].copy_(tb[: n - q * B])
+    lwg.ln_fixed(x, out=x)
+    rows = np.unique(np.concatenate([
+        np.arange(0, 4), np.arange((1 << 29) - 2048, (1 << 29) + 8), np.arange(n - 1100, n),
+        np.random.default_rng(111).choice(n, size=3000, replace=False)]).astype(np.int64))
+    got = take(x, rows)
+    del x
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    assert_ln_close(got, oracle.layer_norm(block[rows % B]), "in-place ln_fixed past 2**32 work-items")
