@@ -20,6 +20,10 @@
  *    stream. Work is enqueued asynchronously; a call returns before it runs.
  *  - Arguments are checked on the host before any HIP call. A non-OK status
  *    means nothing was enqueued; lwg_last_error() then describes the problem.
+ *    Calls return an lwg_status value as int32_t, a type of fixed width for
+ *    callers through a foreign-function interface.
+ *  - eps is a double and enters the binary64 statistics as given (1e-5 is not
+ *    exactly representable, and a float eps would differ from it).
  *  - rows == 0 (or n_out == 0) returns LWG_OK without launching anything; the
  *    pointers are not inspected in that case.
  *  - C = 192 and C = 384 (the model's hidden widths, section 3 of the BW1000
