@@ -23,6 +23,13 @@ from conftest import ROOT
 
 # name -> (file, original text, planted text)
 MISTAKES = {
+    "padding rounds down": ("oracle/window.py", "return -(-extent // window) * window",
+                            "return (extent // window) * window"),
+    "a whole window of padding on exact extents": ("oracle/window.py", "return -(-extent // window) * window",
+                                                   "return (extent // window + 1) * window"),
+    "inverse numbers the gathered rows backwards": ("oracle/window.py",
+                                                    "ids = np.arange(m, dtype=np.int64)[:, None]",
+                                                    "ids = np.arange(m, dtype=np.int64)[::-1, None]"),
     "unbiased variance": ("oracle/rowops.py", "var = (dev * dev).mean(axis=1, keepdims=True)",
                           "var = (dev * dev).sum(axis=1, keepdims=True) / (v.shape[1] - 1)"),
     "eps outside the root": ("oracle/rowops.py", "y = dev / np.sqrt(var + eps)", "y = dev / (np.sqrt(var) + eps)"),
