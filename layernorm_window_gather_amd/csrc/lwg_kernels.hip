@@ -27,7 +27,9 @@
 //     The final binary64 -> binary16 rounding goes through a round-to-odd
 //     binary32 intermediate, which makes the two-step conversion exact-once.
 //   * All kernels are stateless and row-local: no atomics, no scratch memory.
-//     Only the affine kernels use LDS, to hold gamma and beta for a workgroup.
+//     Only the affine kernels use LDS, to hold gamma and beta for a workgroup;
+//     the plain gathers at C = 192 and 768 reserve some, unread, to limit how
+//     many of their workgroups share a compute unit.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -845,6 +847,15 @@ using Streaming = Hints<true, true>;
 //  * C = 768: ln_fixed (150 VGPRs) pipelined at cap 3, -3.4 to -4.5% (cap 2
 //    +1%, cap 4 +10%, uncapped -2%); ln_affine at one tile per wave with load
 //    priority, -1.1 to -1.4% (caps 2-4 +3 to +10%).
+//  * kResident: the plain gather at C = 192 and C = 768 (24 and 36 VGPRs, so
+//    8 waves per SIMD) reserves enough LDS per workgroup, unused, that at most
+//    3 of its workgroups are resident on a compute unit; the grid stays one tile
+//    per wave and the dispatcher starts a workgroup as another ends. With fewer
+//    rows in flight the permuted reads and the writes stream better: C = 192
+//    -5.8 to -6.1% at 131,040 rows and -4.0% at 65,520 (-0.3% at 32,760),
+//    C = 768 -2.3% at 131,040 rows; 4 per CU -4.8% / -1.3%, 5 per CU -4.2% at
+//    C = 192, 2 per CU +3.2%. norm_gather at C = 192 (6 waves per SIMD) and
+//    bias_gelu gained nothing this way (+0.4 to +0.9% and +3.5 to +24%).
 //  * Everything else: the default.
 template <int C, Op O> struct Launch {
     using H = Streaming;
@@ -853,14 +864,17 @@ template <int C, Op O> struct Launch {
     static constexpr int kPriority = 0;
     static constexpr int kChunks = 0;
     static constexpr int kWaves = kBlock / 64;
+    static constexpr int kResident = 0;
 };
-template <int Cap, bool Prefetch, int Priority = 0, int Chunks = 0, int Waves = kBlock / 64> struct Tuned {
+template <int Cap, bool Prefetch, int Priority = 0, int Chunks = 0, int Waves = kBlock / 64, int Resident = 0>
+struct Tuned {
     using H = Streaming;
     static constexpr int kBlocksPerCu = Cap;
     static constexpr bool kPrefetch = Prefetch;
     static constexpr int kPriority = Priority;
     static constexpr int kChunks = Chunks;
     static constexpr int kWaves = Waves;       // waves per workgroup (gathers only)
+    static constexpr int kResident = Resident; // resident workgroups per CU, by LDS (gathers only)
 };
 // Chunks per lane of (width, op): the width's K unless the entry sets kChunks.
 // Only the plain gather may set it, as it copies bits and reduces nothing.
@@ -869,8 +883,9 @@ template <int Cap, bool Prefetch, int Priority = 0, int Chunks = 0, int Waves = 
 template <int C, Op O> constexpr int kChunksOf = Launch<C, O>::kChunks > 0 ? Launch<C, O>::kChunks : Width<C>::K;
 template <int C, Op O>
 constexpr bool kChunksOk = O == Op::kGather || kChunksOf<C, O> == Width<C>::K;
-//                                                  Tuned<cap, pipelined, priority, chunks, waves per workgroup>
+//                                                  Tuned<cap, pipelined, priority, chunks, waves per workgroup, resident>
 template <> struct Launch<192, Op::kLn> : Tuned<4, true> {};
+template <> struct Launch<192, Op::kGather> : Tuned<0, false, 0, 0, 4, 3> {};
 template <> struct Launch<192, Op::kAddLn> : Tuned<3, true> {};
 template <> struct Launch<192, Op::kReverseAddLn> : Tuned<3, true> {};
 template <> struct Launch<192, Op::kAddNormGather> : Tuned<0, true> {};
@@ -886,6 +901,7 @@ template <> struct Launch<384, Op::kLnAffine> : Tuned<4, false> {};
 template <> struct Launch<384, Op::kAddNormGather> : Tuned<4, true> {};
 template <> struct Launch<768, Op::kLn> : Tuned<3, true> {};
 template <> struct Launch<768, Op::kLnAffine> : Tuned<0, false, 1> {};
+template <> struct Launch<768, Op::kGather> : Tuned<0, false, 0, 0, 4, 3> {};
 
 // The caps above were chosen at the model's sizes, where each wave of a capped
 // grid takes 1.1-2.3 row tiles. On larger inputs a capped grid makes every wave
@@ -946,6 +962,8 @@ unsigned grid_for(int64_t rows) {
     static_assert(kChunksOk<C, O>, "a normalising kernel must use its width's chunk count");
     static_assert(O == Op::kGather || O == Op::kNormGather || Launch<C, O>::kWaves == kBlock / 64,
                   "only the gathers take their workgroup size from the launch table");
+    static_assert(O == Op::kGather || O == Op::kNormGather || Launch<C, O>::kResident == 0,
+                  "only the gathers reserve LDS to limit their residency");
     using T = Tile<C, kChunksOf<C, O>>;
     constexpr int kWaves = Launch<C, O>::kWaves;
     const int64_t tiles = (rows + T::kRowsPerWave - 1) / T::kRowsPerWave;
@@ -962,6 +980,17 @@ unsigned grid_for(int64_t rows) {
     constexpr int64_t kMaxBlocks = ((int64_t{1} << 32) - 1) / (64 * kWaves);
     if (blocks > kMaxBlocks) blocks = kMaxBlocks;
     return static_cast<unsigned>(blocks);
+}
+
+// LDS per compute unit on gfx950 (CDNA4).
+constexpr size_t kLdsPerCu = 160 * 1024;
+
+// Dynamic LDS a workgroup of (C, O) reserves so that at most kResident of them
+// fit on a compute unit (0 when the entry sets no limit). No kernel reads it.
+template <int C, Op O>
+constexpr size_t lds_reserve() {
+    constexpr int k = Launch<C, O>::kResident;
+    return k == 0 ? 0 : kLdsPerCu / (k + 1) + 1024;
 }
 
 template <int C>
@@ -988,7 +1017,7 @@ hipError_t gather_c(const void* x, int64_t n_src, const int32_t* table, int64_t 
     constexpr Op O = kNorm ? Op::kNormGather : Op::kGather;
     using L = Launch<C, O>;
     gather_kernel<C, kChunksOf<C, O>, kNorm, typename L::H, L::kPrefetch, L::kWaves, L::kPriority>
-        <<<grid_for<C, O>(n_out), 64 * L::kWaves, 0, s>>>(
+        <<<grid_for<C, O>(n_out), 64 * L::kWaves, lds_reserve<C, O>(), s>>>(
         static_cast<const chunk_t*>(x), n_src, table, n_out, static_cast<chunk_t*>(out), eps);
     return hipGetLastError();
 }
