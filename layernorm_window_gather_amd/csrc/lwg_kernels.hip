@@ -28,8 +28,8 @@
 //     binary32 intermediate, which makes the two-step conversion exact-once.
 //   * All kernels are stateless and row-local: no atomics, no scratch memory.
 //     Only the affine kernels use LDS, to hold gamma and beta for a workgroup;
-//     the plain gathers at C = 192 and 768 reserve some, unread, to limit how
-//     many of their workgroups share a compute unit.
+//     the plain gathers reserve some, unread, to limit how many of their
+//     workgroups share a compute unit.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -841,21 +841,25 @@ using Streaming = Hints<true, true>;
 //    workgroups, so that neighbouring tiles land on different XCDs, was 3-30%
 //    slower on every kernel.)
 //  * C = 384 plain gather: K = 3 (16 lanes per row, 4 rows per wave
-//    instruction) capped at 4 workgroups per compute unit: -2 to -3% against
-//    K = 6 at one tile per wave; caps 2, 3, 5 and 8 and the pipelined loop
-//    measured equal or worse.
+//    instruction). Capped at 4 workgroups per compute unit it was -2 to -3%
+//    against K = 6 at one tile per wave (caps 2, 3, 5 and 8 and the pipelined
+//    loop equal or worse); one tile per wave with 3 resident workgroups per
+//    compute unit (kResident, below) is faster again: -3.6% at 32,760 tokens,
+//    -4.7% and -4.8% at 65,520 and 131,040 (4 resident -2.7%, K = 6 +1.7%).
 //  * C = 768: ln_fixed (150 VGPRs) pipelined at cap 3, -3.4 to -4.5% (cap 2
 //    +1%, cap 4 +10%, uncapped -2%); ln_affine at one tile per wave with load
 //    priority, -1.1 to -1.4% (caps 2-4 +3 to +10%).
-//  * kResident: the plain gather at C = 192 and C = 768 (24 and 36 VGPRs, so
-//    8 waves per SIMD) reserves enough LDS per workgroup, unused, that at most
-//    3 of its workgroups are resident on a compute unit; the grid stays one tile
-//    per wave and the dispatcher starts a workgroup as another ends. With fewer
+//  * kResident: the plain gather at every width (24-36 VGPRs, so 8 waves per
+//    SIMD) reserves enough LDS per workgroup, unused, that at most 3 of its
+//    workgroups are resident on a compute unit; the grid stays one tile per
+//    wave and the dispatcher starts a workgroup as another ends. With fewer
 //    rows in flight the permuted reads and the writes stream better: C = 192
 //    -5.8 to -6.1% at 131,040 rows and -4.0% at 65,520 (-0.3% at 32,760),
 //    C = 768 -2.3% at 131,040 rows; 4 per CU -4.8% / -1.3%, 5 per CU -4.2% at
 //    C = 192, 2 per CU +3.2%. norm_gather at C = 192 (6 waves per SIMD) and
-//    bias_gelu gained nothing this way (+0.4 to +0.9% and +3.5 to +24%).
+//    bias_gelu gained nothing this way (+0.4 to +0.9% and +3.5 to +24%), nor
+//    did ln_affine at C = 192 (+8.3%); add_norm_gather at C = 192 was mixed
+//    (-1.3% at 131,040 rows, +2.8% at 32,760).
 //  * Everything else: the default.
 template <int C, Op O> struct Launch {
     using H = Streaming;
@@ -893,7 +897,7 @@ template <> struct Launch<192, Op::kAddLnAffine> : Tuned<2, true> {};
 template <> struct Launch<192, Op::kLnAffine> : Tuned<0, false, 1> {};
 template <> struct Launch<384, Op::kLn> : Tuned<3, true> {};
 template <> struct Launch<384, Op::kNormGather> : Tuned<12, true, 1, 0, 1> {};
-template <> struct Launch<384, Op::kGather> : Tuned<4, false, 0, 3> {};
+template <> struct Launch<384, Op::kGather> : Tuned<0, false, 0, 3, 4, 3> {};
 template <> struct Launch<384, Op::kAddLn> : Tuned<2, true, 1> {};
 template <> struct Launch<384, Op::kReverseAddLn> : Tuned<2, true, 1> {};
 template <> struct Launch<384, Op::kAddLnAffine> : Tuned<2, true, 1> {};
@@ -912,8 +916,9 @@ template <> struct Launch<768, Op::kGather> : Tuned<0, false, 0, 0, 4, 3> {};
 // tile per wave was 1-10% faster for every kernel; at 65,520 it was faster
 // for norm_gather (-4.4%) and add_norm_gather (-6.0%) at 2.9 and 2.2 tiles per
 // wave, and for add_ln, window_reverse_add_ln and add_ln_affine (-3 to -7%) at
-// 4 tiles per wave, but slower for ln_fixed (+2.0%, 2.7 tiles per wave) and
-// the plain gather (+1.2%, 4.4 tiles per wave). C = 768 ln_fixed on 131,040
+// 4 tiles per wave, but slower for ln_fixed (+2.0%, 2.7 tiles per wave). (The
+// plain gather, then capped, has since gone to one tile per wave at every
+// size.) C = 768 ln_fixed on 131,040
 // rows: -10.4% with the same limit of 3 (its 32,760-row size keeps the cap).
 // The same rule gives C = 192 ln_fixed, add_ln, window_reverse_add_ln and
 // add_ln_affine a cap (4, 3, 3 and 2 workgroups per compute unit) for inputs
@@ -930,7 +935,6 @@ template <> constexpr int kMaxTilesPerWave<384, Op::kAddLnAffine> = 3;
 template <> constexpr int kMaxTilesPerWave<384, Op::kLnAffine> = 3;
 template <> constexpr int kMaxTilesPerWave<384, Op::kNormGather> = 2;
 template <> constexpr int kMaxTilesPerWave<384, Op::kAddNormGather> = 2;
-template <> constexpr int kMaxTilesPerWave<384, Op::kGather> = 5;
 template <> constexpr int kMaxTilesPerWave<768, Op::kLn> = 3;
 template <> constexpr int kMaxTilesPerWave<192, Op::kLn> = 2;
 template <> constexpr int kMaxTilesPerWave<192, Op::kAddLn> = 2;
