@@ -918,8 +918,8 @@ template <> struct Launch<768, Op::kGather> : Tuned<0, false, 0, 0, 4, 3> {};
 // wave, and for add_ln, window_reverse_add_ln and add_ln_affine (-3 to -7%) at
 // 4 tiles per wave, but slower for ln_fixed (+2.0%, 2.7 tiles per wave). (The
 // plain gather, then capped, has since gone to one tile per wave at every
-// size.) C = 768 ln_fixed on 131,040
-// rows: -10.4% with the same limit of 3 (its 32,760-row size keeps the cap).
+// size.) C = 768 ln_fixed on 131,040 rows: -10.4% with the same limit of 3
+// (its 32,760-row size keeps the cap).
 // The same rule gives C = 192 ln_fixed, add_ln, window_reverse_add_ln and
 // add_ln_affine a cap (4, 3, 3 and 2 workgroups per compute unit) for inputs
 // where their waves take at most 2 tiles: -13% (add_ln), -10%
@@ -994,6 +994,8 @@ constexpr size_t kLdsPerCu = 160 * 1024;
 template <int C, Op O>
 constexpr size_t lds_reserve() {
     constexpr int k = Launch<C, O>::kResident;
+    static_assert(k == 0 || kLdsPerCu / (k + 1) + 1024 <= 64 * 1024,
+                  "a reservation stays within the 64 KB a workgroup may request at launch");
     return k == 0 ? 0 : kLdsPerCu / (k + 1) + 1024;
 }
 
