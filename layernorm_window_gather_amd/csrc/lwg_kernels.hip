@@ -20,12 +20,20 @@
 //     lines), and the K instructions of a wave cover 64/LPR full rows.
 //   * Row statistics are reduced across the LPR lanes of a row with DPP
 //     (quad_perm / row_half_mirror / row_mirror), no LDS and no barriers.
-//   * Statistics and the normalisation run in binary64: CDNA4 issues FP64 vector
-//     adds and FMAs at the same per-lane rate as plain FP32, and binary64 makes
-//     each output the correctly rounded binary16 of the exact LayerNorm in
-//     practice, where FP32 arithmetic flips about 1e-4 of outputs by one ulp.
-//     The final binary64 -> binary16 rounding goes through a round-to-odd
-//     binary32 intermediate, which makes the two-step conversion exact-once.
+//   * Statistics and the normalisation run in binary64 (CDNA4 issues FP64 vector
+//     adds and FMAs at the per-lane rate of plain FP32). The sum of a row's
+//     binary16 values is exact in binary64, so the mean is one rounding of the
+//     exact mean. Where the row's mean is within about 3.9 standard deviations
+//     of zero, the variance is taken in the same pass as the sum (mean of
+//     squares minus squared mean, which is well conditioned there) and each
+//     output is fma(x, rstd, -mean*rstd); other rows (near-constant rows, rows
+//     far from zero mean) take a second pass over the deviations and output
+//     (x - mean) * rstd, as the definition reads. Either way each output is the
+//     correctly rounded binary16 of the exact LayerNorm unless the exact value
+//     lies within about 1e-13 (relative) of a rounding midpoint, where FP32
+//     arithmetic would flip about 1e-4 of outputs by one ulp. The final binary64
+//     -> binary16 rounding goes through a round-to-odd binary32 intermediate,
+//     which makes the two-step conversion exact-once.
 //   * All kernels are stateless and row-local: no atomics, no scratch memory.
 //     Only the affine kernels use LDS, to hold gamma and beta for a workgroup;
 //     the plain gathers reserve some, unread, to limit how many of their
@@ -44,7 +52,7 @@ namespace {
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t chunk_t __attribute__((ext_vector_type(4)));  // 16 bytes = 8 x binary16
 
-constexpr int kBlock = 256;  // 4 waves per workgroup
+constexpr int kBlock = 256;  // 4 waves: the workgroup of the table builds and bias_gelu
 
 // Memory hints of a kernel instance: non-temporal loads / stores (the `nt` bit
 // on global_load/global_store: stream through the caches without keeping lines).
@@ -84,10 +92,13 @@ struct Tile {
 // ---------------------------------------------------------------------------
 // Cross-lane sums inside a row group, with DPP
 
+// bound_ctrl is set: the row-local patterns used here (quad_perm, row_half_mirror,
+// row_mirror) read a lane of the same 16-lane row, so no lane is out of range and
+// the instruction needs no "old" operand.
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
     return static_cast<uint32_t>(
-        __builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, true));
 }
 
 template <int CTRL>
@@ -113,13 +124,16 @@ __device__ __forceinline__ double group_sum(double v) {
 // ---------------------------------------------------------------------------
 // Conversions
 
-__device__ __forceinline__ void unpack8(const chunk_t& c, double* out) {
+// The 8 binary16 values of a chunk widened to S (binary32 or binary64; both hold
+// every binary16 value exactly).
+template <class S>
+__device__ __forceinline__ void unpack8(const chunk_t& c, S* out) {
     const uint32_t w[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const half2_t h = __builtin_bit_cast(half2_t, w[i]);
-        out[2 * i] = static_cast<double>(static_cast<float>(h.x));
-        out[2 * i + 1] = static_cast<double>(static_cast<float>(h.y));
+        out[2 * i] = static_cast<S>(static_cast<float>(h.x));
+        out[2 * i + 1] = static_cast<S>(static_cast<float>(h.y));
     }
 }
 
@@ -166,59 +180,118 @@ __device__ __forceinline__ void residual_add(const chunk_t (&branch)[K], chunk_t
     }
 }
 
-// 1/sqrt(a) for a > 0: the hardware reciprocal-square-root estimate refined by
-// one Newton step, r' = r (3/2 - a r^2 / 2), which takes a relative error e to
-// about 1.5 e^2: from the estimate's ~2^-24 to ~2^-47, far below the 2^-11 of a
-// binary16 result. Inf and NaN give NaN.
-__device__ __forceinline__ double rsqrt_refined(double a) {
-    const double r = __builtin_amdgcn_rsq(a);
+// 1/sqrt(a) for a > 0: the hardware reciprocal-square-root estimate (relative
+// error below 2^-24, measured on MI355X) refined by two Newton steps,
+// r' = r (3/2 - a r^2 / 2), each taking a relative error e to about 1.5 e^2:
+// below 2^-47 after the first and at binary64's own rounding level (measured
+// 2^-52.7) after the second. Inf and NaN give NaN.
+__device__ __forceinline__ double newton_rsqrt(double a, double r) {
     const double h = 0.5 * a * r;
     return __builtin_fma(r, __builtin_fma(-h, r, 0.5), r);
 }
 
-// Row statistics of LayerNorm (section 3) for the row whose 1/LPR share this
-// lane holds in v: the mean and the biased variance of the deviations, in two
-// passes over registers. On return x holds this lane's deviations from the mean
-// and the result is 1/sqrt(var + eps).
-template <int C, int K>
-__device__ __forceinline__ double row_stats(const chunk_t (&v)[K], double (&x)[8 * K], double eps) {
-    using T = Tile<C, K>;
-    constexpr double kInvC = 1.0 / C;
-#pragma unroll
-    for (int k = 0; k < K; ++k) unpack8(v[k], x + 8 * k);
-
-    double s0 = 0.0, s1 = 0.0;
-#pragma unroll
-    for (int i = 0; i < T::kValues; i += 2) {
-        s0 += x[i];
-        s1 += x[i + 1];
-    }
-    const double mean = group_sum<T::kLanes>(s0 + s1) * kInvC;
-
-    double q0 = 0.0, q1 = 0.0;
-#pragma unroll
-    for (int i = 0; i < T::kValues; i += 2) {
-        x[i] -= mean;
-        x[i + 1] -= mean;
-        q0 = __builtin_fma(x[i], x[i], q0);
-        q1 = __builtin_fma(x[i + 1], x[i + 1], q1);
-    }
-    return rsqrt_refined(group_sum<T::kLanes>(q0 + q1) * kInvC + eps);
+__device__ __forceinline__ double rsqrt_refined(double a) {
+    return newton_rsqrt(a, newton_rsqrt(a, __builtin_amdgcn_rsq(a)));
 }
 
-// LayerNorm of the row whose 1/LPR share this lane holds in v: (x - mean) /
-// sqrt(var + eps) rounded to binary16, written back into v. Every kernel that
-// normalises a row calls this same function with the same (C, K), so their
-// outputs agree bit for bit.
-template <int C, int K>
+// Row values kept in binary32 between the passes of the LayerNorm are widened
+// to binary64 where each pass uses them. This empty register constraint tells
+// the compiler the values may have changed, so it widens them again instead of
+// keeping a binary64 copy live across the pass (which would double the
+// registers the row takes). Binary64 row values need nothing.
+template <int N>
+__device__ __forceinline__ void rewiden_each_pass(float (&x)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) asm volatile("" : "+v"(x[i]));
+}
+template <int N>
+__device__ __forceinline__ void rewiden_each_pass(double (&)[N]) {}
+
+// Rows whose mean of squares is at most this multiple of their variance (|mean|
+// up to sqrt(15) standard deviations) take the variance from the first pass.
+// The mean of squares carries a relative error of at most ~2^-47 (a sum of at
+// most 48 products per lane, 4 DPP steps and one scaling), so the first-pass
+// variance is good to ~2^-43 there, far below the 2^-11 of a binary16 result.
+constexpr double kOnePassLimit = 16.0;
+
+// Scale of the LayerNorm of the row whose 1/LPR share this lane holds in x:
+// every output is y = fma(x, rstd, shift) with shift = -mean * rstd.
+//  * Rows whose mean is within about 3.9 standard deviations of zero (and
+//    all-zero rows) take the variance from the first pass: the pre-rounding y
+//    has a relative error below ~2^-43.
+//  * Other rows take the variance over the deviations (a second pass). A
+//    constant row has variance exactly 0 (its mean is exact) and gets rstd = 0,
+//    so every output is exactly +0, as (x - mean) / sqrt(eps) is. Any other
+//    binary16 row has |mean| below ~2^15 standard deviations, so rounding
+//    mean * rstd costs at most ~2^-38 of absolute error in y.
+//  * A row holding Inf or NaN gives NaN throughout.
+struct RowScale {
+    double rstd, shift;
+};
+
+template <int C, int K, class S>
+__device__ __forceinline__ RowScale row_scale(S (&x)[8 * K], double eps) {
+    using T = Tile<C, K>;
+    constexpr double kInvC = 1.0 / C;
+    double s0, s1, q0, q1;
+    {
+        const double a = x[0], b = x[1];
+        s0 = a;
+        s1 = b;
+        q0 = a * a;
+        q1 = b * b;
+    }
+#pragma unroll
+    for (int i = 2; i < T::kValues; i += 2) {
+        const double a = x[i], b = x[i + 1];
+        s0 += a;
+        s1 += b;
+        q0 = __builtin_fma(a, a, q0);
+        q1 = __builtin_fma(b, b, q1);
+    }
+    // the sum of binary16 values is a multiple of 2^-24 below 2^26: exact here
+    const double mean = group_sum<T::kLanes>(s0 + s1) * kInvC;
+    const double m2 = group_sum<T::kLanes>(q0 + q1) * kInvC;
+    double var = __builtin_fma(-mean, mean, m2);
+    // all-zero rows (padding) are one-pass too; NaN and Inf rows are not
+    const bool one_pass = (var > 0.0 && m2 <= kOnePassLimit * var) || m2 == 0.0;
+    rewiden_each_pass(x);
+    if (__builtin_amdgcn_ballot_w64(!one_pass) != 0) {
+        double p0 = 0.0, p1 = 0.0;
+#pragma unroll
+        for (int i = 0; i < T::kValues; i += 2) {
+            const double d0 = static_cast<double>(x[i]) - mean;
+            const double d1 = static_cast<double>(x[i + 1]) - mean;
+            p0 = __builtin_fma(d0, d0, p0);
+            p1 = __builtin_fma(d1, d1, p1);
+        }
+        const double var2 = group_sum<T::kLanes>(p0 + p1) * kInvC;
+        if (!one_pass) var = var2;
+        rewiden_each_pass(x);
+    }
+    RowScale rs;
+    rs.rstd = var == 0.0 ? 0.0 : rsqrt_refined(var + eps);
+    rs.shift = -mean * rs.rstd;
+    return rs;
+}
+
+// LayerNorm of the row whose 1/LPR share this lane holds in v, rounded to
+// binary16 and written back into v. S is the register type of the row values
+// between passes (binary32 or binary64; the results do not depend on it). Every
+// kernel that normalises a row calls this same function with its width's
+// (C, K), so their outputs agree bit for bit.
+template <int C, int K, class S>
 __device__ __forceinline__ void layer_norm_lane(chunk_t (&v)[K], double eps) {
-    double x[8 * K];
-    const double rstd = row_stats<C, K>(v, x, eps);
+    S x[8 * K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) unpack8(v[k], x + 8 * k);
+    const RowScale rs = row_scale<C, K>(x, eps);
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-        const double* xk = x + 8 * k;
-        v[k] = chunk_t{pack2(xk[0] * rstd, xk[1] * rstd), pack2(xk[2] * rstd, xk[3] * rstd),
-                       pack2(xk[4] * rstd, xk[5] * rstd), pack2(xk[6] * rstd, xk[7] * rstd)};
+        double y[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = __builtin_fma(static_cast<double>(x[8 * k + e]), rs.rstd, rs.shift);
+        v[k] = chunk_t{pack2(y[0], y[1]), pack2(y[2], y[3]), pack2(y[4], y[5]), pack2(y[6], y[7])};
     }
 }
 
@@ -230,27 +303,27 @@ __device__ __forceinline__ void param_chunk(const double* p, int i, double (&out
     for (int e = 0; e < 8; ++e) out[e] = p[8 * i + e];
 }
 
-// Affine LayerNorm: ((x - mean) / sqrt(var + eps)) * gamma + beta in binary64,
-// rounded once to binary16. gamma and beta are binary16 [C], held in LDS by the
-// affine kernels (as chunks, or widened: P); this lane reads its columns chunk
-// by chunk as it writes them, so only one chunk of them is live next to the
-// row's deviations.
-template <int C, int K, class P>
+// Affine LayerNorm: (normalised x) * gamma + beta in binary64, rounded once to
+// binary16. gamma and beta are binary16 [C], held in LDS by the affine kernels
+// (as chunks, or widened: P); this lane reads its columns chunk by chunk as it
+// writes them, so only one chunk of them is live next to the row values.
+template <int C, int K, class S, class P>
 __device__ __forceinline__ void layer_norm_affine_lane(chunk_t (&v)[K], const P* gamma,
                                                        const P* beta, int sub, double eps) {
     using T = Tile<C, K>;
-    double x[8 * K];
-    const double rstd = row_stats<C, K>(v, x, eps);
+    S x[8 * K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) unpack8(v[k], x + 8 * k);
+    const RowScale rs = row_scale<C, K>(x, eps);
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-        double gk[8], bk[8];
+        double gk[8], bk[8], y[8];
         param_chunk(gamma, sub + k * T::kLanes, gk);
         param_chunk(beta, sub + k * T::kLanes, bk);
-        const double* xk = x + 8 * k;
-        v[k] = chunk_t{pack2(__builtin_fma(xk[0] * rstd, gk[0], bk[0]), __builtin_fma(xk[1] * rstd, gk[1], bk[1])),
-                       pack2(__builtin_fma(xk[2] * rstd, gk[2], bk[2]), __builtin_fma(xk[3] * rstd, gk[3], bk[3])),
-                       pack2(__builtin_fma(xk[4] * rstd, gk[4], bk[4]), __builtin_fma(xk[5] * rstd, gk[5], bk[5])),
-                       pack2(__builtin_fma(xk[6] * rstd, gk[6], bk[6]), __builtin_fma(xk[7] * rstd, gk[7], bk[7]))};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            y[e] = __builtin_fma(__builtin_fma(static_cast<double>(x[8 * k + e]), rs.rstd, rs.shift), gk[e], bk[e]);
+        v[k] = chunk_t{pack2(y[0], y[1]), pack2(y[2], y[3]), pack2(y[4], y[5]), pack2(y[6], y[7])};
     }
 }
 
@@ -267,7 +340,7 @@ __device__ __forceinline__ void zero(chunk_t (&v)[K]) {
 // is the kRowsPerWave rows one wave covers. The loop bound is the same for every
 // lane of a wave, so the DPP reductions always run with the whole wave active.
 // The launcher sizes the grid either to one tile per wave or to a fixed number
-// of resident workgroups.
+// of resident workgroups. kWaves is the number of waves in a workgroup.
 
 template <int kWaves>
 __device__ __forceinline__ int64_t first_wave_in() {
@@ -278,11 +351,6 @@ template <int kWaves>
 __device__ __forceinline__ int64_t wave_stride_in() {
     return static_cast<int64_t>(gridDim.x) * kWaves;
 }
-
-// For kernels launched with kBlock threads per workgroup (all but the gathers,
-// whose workgroup size is a launch-table choice).
-__device__ __forceinline__ int64_t first_wave() { return first_wave_in<kBlock / 64>(); }
-__device__ __forceinline__ int64_t wave_stride() { return wave_stride_in<kBlock / 64>(); }
 
 // The K chunks this lane holds of row tile w (zeros past the last row). With
 // kPrio > 0 the wave issues the loads at that scheduling priority (s_setprio)
@@ -322,55 +390,44 @@ __device__ __forceinline__ void store_tile(chunk_t* y, int64_t w, int64_t rows, 
 // traffic of the next. (In place, the next tile's rows are other rows, read
 // before this tile's stores: still no overlap between a lane's reads and
 // another lane's writes.)
-template <int C, int K, class H, bool kPrefetch>
-__global__ __launch_bounds__(kBlock) void ln_fixed_kernel(const chunk_t* x, chunk_t* y,
-                                                          int64_t rows, double eps) {
+template <int C, int K, class H, bool kPrefetch, int kPrio, int kWaves, class S>
+__global__ __launch_bounds__(64 * kWaves) void ln_fixed_kernel(const chunk_t* x, chunk_t* y,
+                                                               int64_t rows, double eps) {
     using T = Tile<C, K>;
     const int lane = threadIdx.x & 63;
+    const int64_t stride = wave_stride_in<kWaves>();
+    int64_t w = first_wave_in<kWaves>();
     if constexpr (kPrefetch) {
-        const int64_t stride = wave_stride();
-        int64_t w = first_wave();
         chunk_t v[K];
-        load_tile<C, K, H>(x, w, rows, lane, v);
+        load_tile<C, K, H, kPrio>(x, w, rows, lane, v);
         for (; w * T::kRowsPerWave < rows; w += stride) {
             chunk_t next[K];
-            load_tile<C, K, H>(x, w + stride, rows, lane, next);
-            layer_norm_lane<C, K>(v, eps);
+            load_tile<C, K, H, kPrio>(x, w + stride, rows, lane, next);
+            layer_norm_lane<C, K, S>(v, eps);
             store_tile<C, K, H>(y, w, rows, lane, v);
 #pragma unroll
             for (int k = 0; k < K; ++k) v[k] = next[k];
         }
     } else {
-        const int sub = lane % T::kLanes;
-        for (int64_t w = first_wave(); w * T::kRowsPerWave < rows; w += wave_stride()) {
-            const int64_t row = w * T::kRowsPerWave + lane / T::kLanes;
-            const bool live = row < rows;
-            const int64_t base = row * T::kChunks + sub;
+        for (; w * T::kRowsPerWave < rows; w += stride) {
             chunk_t v[K];
-            zero(v);
-            if (live) {
-#pragma unroll
-                for (int k = 0; k < K; ++k) v[k] = load16<H>(x + base + k * T::kLanes);
-            }
-            layer_norm_lane<C, K>(v, eps);
-            if (live) {
-#pragma unroll
-                for (int k = 0; k < K; ++k) store16<H>(y + base + k * T::kLanes, v[k]);
-            }
+            load_tile<C, K, H, kPrio>(x, w, rows, lane, v);
+            layer_norm_lane<C, K, S>(v, eps);
+            store_tile<C, K, H>(y, w, rows, lane, v);
         }
     }
 }
 
 // residual_out and y may alias the inputs: each lane reads its chunks of a row
 // before it writes any, and the prefetched tile is a different set of rows.
-template <int C, int K, class H, bool kPrefetch, int kPrio>
-__global__ __launch_bounds__(kBlock) void add_ln_kernel(const chunk_t* branch, const chunk_t* residual,
-                                                        chunk_t* residual_out, chunk_t* y,
-                                                        int64_t rows, double eps) {
+template <int C, int K, class H, bool kPrefetch, int kPrio, int kWaves, class S>
+__global__ __launch_bounds__(64 * kWaves) void add_ln_kernel(const chunk_t* branch, const chunk_t* residual,
+                                                             chunk_t* residual_out, chunk_t* y,
+                                                             int64_t rows, double eps) {
     using T = Tile<C, K>;
     const int lane = threadIdx.x & 63;
-    const int64_t stride = wave_stride();
-    int64_t w = first_wave();
+    const int64_t stride = wave_stride_in<kWaves>();
+    int64_t w = first_wave_in<kWaves>();
     chunk_t b[K], r[K];
     load_tile<C, K, H, kPrio>(branch, w, rows, lane, b);
     load_tile<C, K, H, kPrio>(residual, w, rows, lane, r);
@@ -382,7 +439,7 @@ __global__ __launch_bounds__(kBlock) void add_ln_kernel(const chunk_t* branch, c
         }
         residual_add<K>(b, r);
         store_tile<C, K, H>(residual_out, w, rows, lane, r);
-        layer_norm_lane<C, K>(r, eps);
+        layer_norm_lane<C, K, S>(r, eps);
         store_tile<C, K, H>(y, w, rows, lane, r);
         if constexpr (kPrefetch) {
 #pragma unroll
@@ -414,7 +471,7 @@ struct AffineStage {
 template <int C>
 __device__ __forceinline__ void stage_params(chunk_t* params, const chunk_t* gamma, const chunk_t* beta) {
     constexpr int kChunks = C / 8;
-    for (int i = threadIdx.x; i < 2 * kChunks; i += kBlock)
+    for (int i = threadIdx.x; i < 2 * kChunks; i += blockDim.x)
         params[i] = i < kChunks ? gamma[i] : beta[i - kChunks];
     __syncthreads();
 }
@@ -422,7 +479,7 @@ __device__ __forceinline__ void stage_params(chunk_t* params, const chunk_t* gam
 template <int C>
 __device__ __forceinline__ void stage_params(double* params, const chunk_t* gamma, const chunk_t* beta) {
     constexpr int kChunks = C / 8;
-    for (int i = threadIdx.x; i < 2 * kChunks; i += kBlock) {
+    for (int i = threadIdx.x; i < 2 * kChunks; i += blockDim.x) {
         double v[8];
         unpack8(i < kChunks ? gamma[i] : beta[i - kChunks], v);
 #pragma unroll
@@ -431,47 +488,54 @@ __device__ __forceinline__ void stage_params(double* params, const chunk_t* gamm
     __syncthreads();
 }
 
-template <int C, int K, class H, int kPrio, bool kWide>
-__global__ __launch_bounds__(kBlock) void ln_affine_kernel(const chunk_t* x, const chunk_t* gamma,
-                                                           const chunk_t* beta, chunk_t* y,
-                                                           int64_t rows, double eps) {
+template <int C, int K, class H, bool kPrefetch, int kPrio, int kWaves, class S, bool kWide>
+__global__ __launch_bounds__(64 * kWaves) void ln_affine_kernel(const chunk_t* x, const chunk_t* gamma,
+                                                                const chunk_t* beta, chunk_t* y,
+                                                                int64_t rows, double eps) {
     using T = Tile<C, K>;
-    using S = AffineStage<C, kWide>;
-    __shared__ typename S::P params[2 * S::kHalf];
+    using A = AffineStage<C, kWide>;
+    __shared__ typename A::P params[2 * A::kHalf];
     stage_params<C>(params, gamma, beta);
-    const typename S::P* gamma_s = params;
-    const typename S::P* beta_s = params + S::kHalf;
+    const typename A::P* gamma_s = params;
+    const typename A::P* beta_s = params + A::kHalf;
     const int lane = threadIdx.x & 63;
     const int sub = lane % T::kLanes;
-    const int64_t stride = wave_stride();
-    int64_t w = first_wave();
+    const int64_t stride = wave_stride_in<kWaves>();
+    int64_t w = first_wave_in<kWaves>();
     chunk_t v[K];
     load_tile<C, K, H, kPrio>(x, w, rows, lane, v);
     for (; w * T::kRowsPerWave < rows; w += stride) {
+        chunk_t next[K];
+        if constexpr (kPrefetch) load_tile<C, K, H, kPrio>(x, w + stride, rows, lane, next);
         // re-read gamma/beta from LDS per row tile instead of letting the
         // compiler hoist 2*K widened chunks out of the loop into registers
         asm volatile("" ::: "memory");
-        layer_norm_affine_lane<C, K>(v, gamma_s, beta_s, sub, eps);
+        layer_norm_affine_lane<C, K, S>(v, gamma_s, beta_s, sub, eps);
         store_tile<C, K, H>(y, w, rows, lane, v);
-        load_tile<C, K, H, kPrio>(x, w + stride, rows, lane, v);
+        if constexpr (kPrefetch) {
+#pragma unroll
+            for (int k = 0; k < K; ++k) v[k] = next[k];
+        } else {
+            load_tile<C, K, H, kPrio>(x, w + stride, rows, lane, v);
+        }
     }
 }
 
-template <int C, int K, class H, bool kPrefetch, int kPrio, bool kWide>
-__global__ __launch_bounds__(kBlock) void add_ln_affine_kernel(const chunk_t* branch, const chunk_t* residual,
-                                                                 const chunk_t* gamma, const chunk_t* beta,
-                                                                 chunk_t* residual_out, chunk_t* y,
-                                                                 int64_t rows, double eps) {
+template <int C, int K, class H, bool kPrefetch, int kPrio, int kWaves, class S, bool kWide>
+__global__ __launch_bounds__(64 * kWaves) void add_ln_affine_kernel(const chunk_t* branch, const chunk_t* residual,
+                                                                    const chunk_t* gamma, const chunk_t* beta,
+                                                                    chunk_t* residual_out, chunk_t* y,
+                                                                    int64_t rows, double eps) {
     using T = Tile<C, K>;
-    using S = AffineStage<C, kWide>;
-    __shared__ typename S::P params[2 * S::kHalf];
+    using A = AffineStage<C, kWide>;
+    __shared__ typename A::P params[2 * A::kHalf];
     stage_params<C>(params, gamma, beta);
-    const typename S::P* gamma_s = params;
-    const typename S::P* beta_s = params + S::kHalf;
+    const typename A::P* gamma_s = params;
+    const typename A::P* beta_s = params + A::kHalf;
     const int lane = threadIdx.x & 63;
     const int sub = lane % T::kLanes;
-    const int64_t stride = wave_stride();
-    int64_t w = first_wave();
+    const int64_t stride = wave_stride_in<kWaves>();
+    int64_t w = first_wave_in<kWaves>();
     chunk_t b[K], r[K];
     load_tile<C, K, H, kPrio>(branch, w, rows, lane, b);
     load_tile<C, K, H, kPrio>(residual, w, rows, lane, r);
@@ -484,7 +548,7 @@ __global__ __launch_bounds__(kBlock) void add_ln_affine_kernel(const chunk_t* br
         asm volatile("" ::: "memory");  // as in ln_affine_kernel: no hoisting of gamma/beta
         residual_add<K>(b, r);
         store_tile<C, K, H>(residual_out, w, rows, lane, r);
-        layer_norm_affine_lane<C, K>(r, gamma_s, beta_s, sub, eps);
+        layer_norm_affine_lane<C, K, S>(r, gamma_s, beta_s, sub, eps);
         store_tile<C, K, H>(y, w, rows, lane, r);
         if constexpr (kPrefetch) {
 #pragma unroll
@@ -520,7 +584,7 @@ __device__ __forceinline__ void load_gathered(const chunk_t* x, int64_t n_src, c
     if constexpr (kPrio > 0) __builtin_amdgcn_s_setprio(0);
 }
 
-template <int C, int K, bool kNorm, class H, bool kPrefetch, int kWaves, int kPrio>
+template <int C, int K, bool kNorm, class H, bool kPrefetch, int kWaves, int kPrio, class S>
 __global__ __launch_bounds__(64 * kWaves) void gather_kernel(const chunk_t* __restrict__ x, int64_t n_src,
                                                              const int32_t* __restrict__ table,
                                                              int64_t n_out, chunk_t* __restrict__ out,
@@ -535,7 +599,7 @@ __global__ __launch_bounds__(64 * kWaves) void gather_kernel(const chunk_t* __re
         for (; w * T::kRowsPerWave < n_out; w += stride) {
             chunk_t next[K];
             load_gathered<C, K, H, kPrio>(x, n_src, table, n_out, w + stride, lane, next);
-            if constexpr (kNorm) layer_norm_lane<C, K>(v, eps);
+            if constexpr (kNorm) layer_norm_lane<C, K, S>(v, eps);
             store_tile<C, K, H>(out, w, n_out, lane, v);
 #pragma unroll
             for (int k = 0; k < K; ++k) v[k] = next[k];
@@ -556,12 +620,54 @@ __global__ __launch_bounds__(64 * kWaves) void gather_kernel(const chunk_t* __re
                 for (int k = 0; k < K; ++k) v[k] = load16<H>(x + src + k * T::kLanes);
             }
             if constexpr (kPrio > 0) __builtin_amdgcn_s_setprio(0);
-            if constexpr (kNorm) layer_norm_lane<C, K>(v, eps);
+            if constexpr (kNorm) layer_norm_lane<C, K, S>(v, eps);
             if (live) {
                 const int64_t dst = j * T::kChunks + sub;
 #pragma unroll
                 for (int k = 0; k < K; ++k) store16<H>(out + dst + k * T::kLanes, v[k]);
             }
+        }
+    }
+}
+
+// Plain gather with kTiles row tiles per wave (tiles g + i * (waves in the
+// grid)): the wave reads all of its table entries first, then the source rows
+// of every tile, then stores them, so each wave has all of its loads in flight
+// before the first store. The grid has ceil(tiles / kTiles) waves.
+template <int C, int K, class H, int kTiles, int kWaves, int kPrio>
+__global__ __launch_bounds__(64 * kWaves) void gather_tiles_kernel(const chunk_t* __restrict__ x, int64_t n_src,
+                                                                   const int32_t* __restrict__ table,
+                                                                   int64_t n_out, chunk_t* __restrict__ out) {
+    using T = Tile<C, K>;
+    const int lane = threadIdx.x & 63;
+    const int sub = lane % T::kLanes;
+    const int64_t g = first_wave_in<kWaves>();
+    const int64_t waves = wave_stride_in<kWaves>();
+    int64_t j[kTiles];
+    int32_t t[kTiles];
+    if constexpr (kPrio > 0) __builtin_amdgcn_s_setprio(kPrio);
+#pragma unroll
+    for (int i = 0; i < kTiles; ++i) {
+        j[i] = (g + i * waves) * T::kRowsPerWave + lane / T::kLanes;
+        t[i] = j[i] < n_out ? table[j[i]] : -1;
+    }
+    chunk_t v[kTiles][K];
+#pragma unroll
+    for (int i = 0; i < kTiles; ++i) {
+        zero(v[i]);
+        if (t[i] >= 0 && static_cast<int64_t>(t[i]) < n_src) {
+            const int64_t src = static_cast<int64_t>(t[i]) * T::kChunks + sub;
+#pragma unroll
+            for (int k = 0; k < K; ++k) v[i][k] = load16<H>(x + src + k * T::kLanes);
+        }
+    }
+    if constexpr (kPrio > 0) __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+    for (int i = 0; i < kTiles; ++i) {
+        if (j[i] < n_out) {
+            const int64_t dst = j[i] * T::kChunks + sub;
+#pragma unroll
+            for (int k = 0; k < K; ++k) store16<H>(out + dst + k * T::kLanes, v[i][k]);
         }
     }
 }
@@ -572,26 +678,26 @@ __global__ __launch_bounds__(64 * kWaves) void gather_kernel(const chunk_t* __re
 // a zero branch. residual_out and y may alias residual (row i is read and
 // written by the same lanes; a prefetched tile holds other rows); neither may
 // overlap win, whose rows a prefetch may read after another row was written.
-template <int C, int K, class H, bool kPrefetch, int kPrio>
-__global__ __launch_bounds__(kBlock) void reverse_add_ln_kernel(
+template <int C, int K, class H, bool kPrefetch, int kPrio, int kWaves, class S>
+__global__ __launch_bounds__(64 * kWaves) void reverse_add_ln_kernel(
     const chunk_t* __restrict__ win, int64_t n_win, const int32_t* __restrict__ idx,
     const chunk_t* residual, chunk_t* residual_out, chunk_t* y, int64_t rows, double eps) {
     using T = Tile<C, K>;
     const int lane = threadIdx.x & 63;
-    const int64_t stride = wave_stride();
-    int64_t w = first_wave();
+    const int64_t stride = wave_stride_in<kWaves>();
+    int64_t w = first_wave_in<kWaves>();
     chunk_t b[K], r[K];
-    load_gathered<C, K, H>(win, n_win, idx, rows, w, lane, b);
+    load_gathered<C, K, H, kPrio>(win, n_win, idx, rows, w, lane, b);
     load_tile<C, K, H, kPrio>(residual, w, rows, lane, r);
     for (; w * T::kRowsPerWave < rows; w += stride) {
         chunk_t nb[K], nr[K];
         if constexpr (kPrefetch) {
-            load_gathered<C, K, H>(win, n_win, idx, rows, w + stride, lane, nb);
+            load_gathered<C, K, H, kPrio>(win, n_win, idx, rows, w + stride, lane, nb);
             load_tile<C, K, H, kPrio>(residual, w + stride, rows, lane, nr);
         }
         residual_add<K>(b, r);
         store_tile<C, K, H>(residual_out, w, rows, lane, r);
-        layer_norm_lane<C, K>(r, eps);
+        layer_norm_lane<C, K, S>(r, eps);
         store_tile<C, K, H>(y, w, rows, lane, r);
         if constexpr (kPrefetch) {
 #pragma unroll
@@ -600,7 +706,7 @@ __global__ __launch_bounds__(kBlock) void reverse_add_ln_kernel(
                 r[k] = nr[k];
             }
         } else {
-            load_gathered<C, K, H>(win, n_win, idx, rows, w + stride, lane, b);
+            load_gathered<C, K, H, kPrio>(win, n_win, idx, rows, w + stride, lane, b);
             load_tile<C, K, H, kPrio>(residual, w + stride, rows, lane, r);
         }
     }
@@ -608,11 +714,12 @@ __global__ __launch_bounds__(kBlock) void reverse_add_ln_kernel(
 
 // Branch and residual chunks of the source row of gathered row j (zeros and -1
 // for padding or an out-of-range entry); returns the source row or -1.
-template <int C, int K, class H>
+template <int C, int K, class H, int kPrio>
 __device__ __forceinline__ int32_t load_pair(const chunk_t* branch, const chunk_t* residual, int64_t n_src,
                                              const int32_t* table, int64_t n_out, int64_t w, int lane,
                                              chunk_t (&b)[K], chunk_t (&r)[K]) {
     using T = Tile<C, K>;
+    if constexpr (kPrio > 0) __builtin_amdgcn_s_setprio(kPrio);
     const int64_t j = w * T::kRowsPerWave + lane / T::kLanes;
     int32_t t = j < n_out ? table[j] : -1;
     if (!(t >= 0 && static_cast<int64_t>(t) < n_src)) t = -1;
@@ -626,6 +733,7 @@ __device__ __forceinline__ int32_t load_pair(const chunk_t* branch, const chunk_
             r[k] = load16<H>(residual + src + k * T::kLanes);
         }
     }
+    if constexpr (kPrio > 0) __builtin_amdgcn_s_setprio(0);
     return t;
 }
 
@@ -636,29 +744,29 @@ __device__ __forceinline__ int32_t load_pair(const chunk_t* branch, const chunk_
 // window_index_kernel) every token row is read and written by exactly one lane
 // group, and a prefetched tile reads other tokens than the one being written,
 // so residual_out may alias residual or branch.
-template <int C, int K, class H, bool kPrefetch>
-__global__ __launch_bounds__(kBlock) void add_norm_gather_kernel(
+template <int C, int K, class H, bool kPrefetch, int kPrio, int kWaves, class S>
+__global__ __launch_bounds__(64 * kWaves) void add_norm_gather_kernel(
     const chunk_t* branch, const chunk_t* residual, chunk_t* residual_out, int64_t n_src,
     const int32_t* __restrict__ table, int64_t n_out, chunk_t* __restrict__ out, double eps) {
     using T = Tile<C, K>;
     const int lane = threadIdx.x & 63;
     const int sub = lane % T::kLanes;
-    const int64_t stride = wave_stride();
-    int64_t w = first_wave();
+    const int64_t stride = wave_stride_in<kWaves>();
+    int64_t w = first_wave_in<kWaves>();
     chunk_t b[K], r[K];
-    int32_t t = load_pair<C, K, H>(branch, residual, n_src, table, n_out, w, lane, b, r);
+    int32_t t = load_pair<C, K, H, kPrio>(branch, residual, n_src, table, n_out, w, lane, b, r);
     for (; w * T::kRowsPerWave < n_out; w += stride) {
         chunk_t nb[K], nr[K];
         int32_t nt = -1;
         if constexpr (kPrefetch)
-            nt = load_pair<C, K, H>(branch, residual, n_src, table, n_out, w + stride, lane, nb, nr);
+            nt = load_pair<C, K, H, kPrio>(branch, residual, n_src, table, n_out, w + stride, lane, nb, nr);
         residual_add<K>(b, r);
         if (t >= 0) {
             const int64_t src = static_cast<int64_t>(t) * T::kChunks + sub;
 #pragma unroll
             for (int k = 0; k < K; ++k) store16<H>(residual_out + src + k * T::kLanes, r[k]);
         }
-        layer_norm_lane<C, K>(r, eps);
+        layer_norm_lane<C, K, S>(r, eps);
         store_tile<C, K, H>(out, w, n_out, lane, r);
         if constexpr (kPrefetch) {
 #pragma unroll
@@ -668,7 +776,7 @@ __global__ __launch_bounds__(kBlock) void add_norm_gather_kernel(
             }
             t = nt;
         } else {
-            t = load_pair<C, K, H>(branch, residual, n_src, table, n_out, w + stride, lane, b, r);
+            t = load_pair<C, K, H, kPrio>(branch, residual, n_src, table, n_out, w + stride, lane, b, r);
         }
     }
 }
@@ -764,6 +872,7 @@ __global__ __launch_bounds__(kBlock) void bias_gelu_kernel(const f32x4_t* x, con
     }
 }
 
+
 // ---------------------------------------------------------------------------
 // Launch configuration
 
@@ -779,18 +888,12 @@ __global__ __launch_bounds__(kBlock) void bias_gelu_kernel(const f32x4_t* x, con
 // 16 lanes per row, 256 contiguous bytes of each of 4 rows per instruction.
 // Every kernel streams its inputs once and never re-reads its outputs, so all
 // loads and stores carry the non-temporal hint; on cold data that beat plain
-// and store-only-hinted accesses for every kernel. The grid is one tile per
-// wave unless the table of Launch entries below says otherwise. (K = 3 at
-// C = 384, 16 lanes per row, measured -2% on the gathers and +5% / +16% on
-// ln_fixed / ln_affine; the normalising kernels keep K = 6 so that all of them
-// reduce a row alike, and only the plain gather takes K = 3.)
+// and store-only-hinted accesses for every kernel.
 enum class Op { kLn, kAddLn, kGather, kNormGather, kReverseAddLn, kAddNormGather, kLnAffine, kAddLnAffine };
 
 template <int C> struct Width;
 // kWideParams: the affine kernels stage gamma and beta in LDS widened to
-// binary64. Measured against binary16 staging: C = 384 ln_affine -2.8%,
-// add_ln_affine -2.1%; C = 192 +1.2% / +1.0% and C = 768 ln_affine +4.3%, so
-// only C = 384 takes it.
+// binary64 (C = 384), or as the binary16 chunks (C = 192 and 768).
 template <> struct Width<192> { static constexpr int K = 3; static constexpr bool kWideParams = false; };
 template <> struct Width<384> { static constexpr int K = 6; static constexpr bool kWideParams = true; };
 // the patch-merge width: 16 lanes per row, 6 chunks each (whole 256-byte pieces
@@ -799,148 +902,114 @@ template <> struct Width<768> { static constexpr int K = 6; static constexpr boo
 
 using Streaming = Hints<true, true>;
 
-// Per (width, op): kBlocksPerCu caps the grid at that many workgroups per
-// compute unit (0 = one tile per wave); kPrefetch selects the software-pipelined
-// row loop (the next tile's loads issued before the current tile is
-// normalised); kPriority, kChunks and kWaves are described below. Each entry
-// was measured against the alternatives on cold buffers, in interleaved runs on
-// one MI355X:
-//  * C = 384: with a cap each wave takes 1.3-2.3 tiles and, pipelined,
-//    normalises one while the next loads: ln_fixed -11%, norm_gather -10%,
-//    add_ln -4%, window_reverse_add_ln -4%, add_ln_affine -6%; ln_affine gains
-//    from the cap alone (it loses with the pipeline): cap 3 at first (-9%),
-//    cap 4 since its parameters are widened in LDS (128 VGPRs, 4 waves per
-//    SIMD; -4% against cap 3, and cap 4 with priority -3%). Register counts
-//    (the compiler's NumVgprs) set how many waves are resident, and these caps
-//    fill exactly that: the single-input pipelined kernels hold 150-156 VGPRs
-//    (3 waves per SIMD) and take cap 3; add_ln, window_reverse_add_ln and
-//    add_ln_affine hold 180-194 (2 waves per SIMD) and take cap 2, caps 3 and
-//    4 (a second generation of workgroups) measuring 3-16% slower.
-//    add_norm_gather (188 VGPRs) is the exception: fastest pipelined at cap 4,
-//    -3.4% against cap 2 without the pipeline. Halving the registers (each
-//    pass re-widening the binary16 values instead of keeping the binary64
-//    deviations) raised residency and made every LayerNorm kernel slower,
-//    +3-7% at C = 192 and +13-23% at C = 384, with or without larger caps.
-//  * C = 192, one tile per wave: the pipelined form of ln_fixed, add_ln and the
-//    fused residual kernels issues the tile's loads ahead of the loop test and
-//    measured 2-4% faster; the gathers and ln_affine are fastest as they are.
-//    (ln_fixed, add_ln, window_reverse_add_ln and add_ln_affine carry caps
-//    that apply only to inputs smaller than the model's; see kMaxTilesPerWave
-//    below.)
-//  * kPriority: the pipelined two-input kernels at C = 384 and ln_affine at
-//    C = 192 issue their loads at wave priority 1 (s_setprio) and drop to 0
-//    for the arithmetic: C = 384 add_ln -7%, add_ln_affine -5%,
-//    window_reverse_add_ln -1%, C = 192 ln_affine -2.5%. On the one-tile-per-
-//    wave kernels it cost up to 4% and is off. The C = 384 norm_gather took it
-//    once it ran one-wave workgroups (-2.5 to -2.8%; with four-wave workgroups
-//    it had been neutral).
-//  * C = 384 norm_gather runs one wave per workgroup, 12 workgroups per
-//    compute unit (the same 12 waves as 3 four-wave workgroups): -1.9%. Caps
-//    of 8, 16 and 24 one-wave workgroups, the loop without the pipeline, and
-//    one tile per wave measured 6-16% slower. (Numbering the waves across
-//    workgroups, so that neighbouring tiles land on different XCDs, was 3-30%
-//    slower on every kernel.)
-//  * C = 384 plain gather: K = 3 (16 lanes per row, 4 rows per wave
-//    instruction). Capped at 4 workgroups per compute unit it was -2 to -3%
-//    against K = 6 at one tile per wave (caps 2, 3, 5 and 8 and the pipelined
-//    loop equal or worse); one tile per wave with 3 resident workgroups per
-//    compute unit (kResident, below) is faster again: -3.6% at 32,760 tokens,
-//    -4.7% and -4.8% at 65,520 and 131,040 (4 resident -2.7%, K = 6 +1.7%).
-//  * C = 768: ln_fixed (150 VGPRs) pipelined at cap 3, -3.4 to -4.5% (cap 2
-//    +1%, cap 4 +10%, uncapped -2%); ln_affine at one tile per wave with load
-//    priority, -1.1 to -1.4% (caps 2-4 +3 to +10%).
-//  * kResident: the plain gather at every width (24-36 VGPRs, so 8 waves per
-//    SIMD) reserves enough LDS per workgroup, unused, that at most 3 of its
-//    workgroups are resident on a compute unit; the grid stays one tile per
-//    wave and the dispatcher starts a workgroup as another ends. With fewer
-//    rows in flight the permuted reads and the writes stream better: C = 192
-//    -5.8 to -6.1% at 131,040 rows and -4.0% at 65,520 (-0.3% at 32,760),
-//    C = 768 -2.3% at 131,040 rows; 4 per CU -4.8% / -1.3%, 5 per CU -4.2% at
-//    C = 192, 2 per CU +3.2%. norm_gather at C = 192 (6 waves per SIMD) and
-//    bias_gelu gained nothing this way (+0.4 to +0.9% and +3.5 to +24%), nor
-//    did ln_affine at C = 192 (+8.3%); add_norm_gather at C = 192 was mixed
-//    (-1.3% at 131,040 rows, +2.8% at 32,760).
-//  * Everything else: the default.
+// Per (width, op):
+//  * kBlocksPerCu caps the grid at that many workgroups per compute unit
+//    (0 = one tile per wave, or kTiles tiles per wave);
+//  * kPrefetch selects the software-pipelined row loop (the next tile's loads
+//    issued before the current tile is normalised);
+//  * kPriority > 0 issues the loads at that wave priority (s_setprio) and drops
+//    to 0 for the arithmetic and the stores;
+//  * kWaves is the workgroup size in waves;
+//  * Row is the register type of a row between the passes of the LayerNorm:
+//    double, or float (exact for binary16, widened again in each pass: one
+//    conversion more per value and pass, half the registers);
+//  * kResident reserves enough LDS per workgroup, unread, that at most that
+//    many workgroups are resident on a compute unit;
+//  * kChunks overrides K (plain gather only: it reduces nothing);
+//  * kTiles > 1 gives each wave that many tiles, all loads first (plain gather
+//    only).
 template <int C, Op O> struct Launch {
     using H = Streaming;
+    using Row = double;
     static constexpr int kBlocksPerCu = 0;
     static constexpr bool kPrefetch = false;
     static constexpr int kPriority = 0;
-    static constexpr int kChunks = 0;
-    static constexpr int kWaves = kBlock / 64;
+    static constexpr int kWaves = 4;
     static constexpr int kResident = 0;
+    static constexpr int kChunks = 0;
+    static constexpr int kTiles = 1;
 };
-template <int Cap, bool Prefetch, int Priority = 0, int Chunks = 0, int Waves = kBlock / 64, int Resident = 0>
+template <int Cap, bool Prefetch, int Priority = 0, int Waves = 4, class R = double, int Resident = 0,
+          int Chunks = 0, int Tiles = 1>
 struct Tuned {
     using H = Streaming;
+    using Row = R;
     static constexpr int kBlocksPerCu = Cap;
     static constexpr bool kPrefetch = Prefetch;
     static constexpr int kPriority = Priority;
+    static constexpr int kWaves = Waves;
+    static constexpr int kResident = Resident;
     static constexpr int kChunks = Chunks;
-    static constexpr int kWaves = Waves;       // waves per workgroup (gathers only)
-    static constexpr int kResident = Resident; // resident workgroups per CU, by LDS (gathers only)
+    static constexpr int kTiles = Tiles;
 };
 // Chunks per lane of (width, op): the width's K unless the entry sets kChunks.
-// Only the plain gather may set it, as it copies bits and reduces nothing.
-// Every normalising kernel of a width keeps Width<C>::K, so they all reduce a
-// row in the same order.
 template <int C, Op O> constexpr int kChunksOf = Launch<C, O>::kChunks > 0 ? Launch<C, O>::kChunks : Width<C>::K;
 template <int C, Op O>
 constexpr bool kChunksOk = O == Op::kGather || kChunksOf<C, O> == Width<C>::K;
-//                                                  Tuned<cap, pipelined, priority, chunks, waves per workgroup, resident>
+
+// Level 1 (C = 192, 131,040 rows): every kernel holds its row in binary64.
+//  * ln_fixed, add_ln and the fused residual kernels: the pipelined loop, which
+//    issues a tile's loads ahead of the loop test (2-4% faster than the plain
+//    loop at one tile per wave); their caps apply only below the model's size
+//    (kMaxTilesPerWave).
+//  * plain gather: one tile per wave with at most 3 resident workgroups per
+//    compute unit (-6% against no limit: fewer rows in flight stream better).
+//  * norm_gather: one tile per wave in 4-wave workgroups, at most 6 resident
+//    per compute unit (its 70 registers would allow 7: -1.5%).
+//  * ln_affine: one tile per wave with load priority.
+//                                                  Tuned<cap, pipelined, priority, waves, row, resident, chunks, tiles>
 template <> struct Launch<192, Op::kLn> : Tuned<4, true> {};
-template <> struct Launch<192, Op::kGather> : Tuned<0, false, 0, 0, 4, 3> {};
+template <> struct Launch<192, Op::kGather> : Tuned<0, false, 0, 4, double, 3> {};
+template <> struct Launch<192, Op::kNormGather> : Tuned<0, false, 0, 4, double, 6> {};
 template <> struct Launch<192, Op::kAddLn> : Tuned<3, true> {};
 template <> struct Launch<192, Op::kReverseAddLn> : Tuned<3, true> {};
 template <> struct Launch<192, Op::kAddNormGather> : Tuned<0, true> {};
 template <> struct Launch<192, Op::kAddLnAffine> : Tuned<2, true> {};
 template <> struct Launch<192, Op::kLnAffine> : Tuned<0, false, 1> {};
-template <> struct Launch<384, Op::kLn> : Tuned<3, true> {};
-template <> struct Launch<384, Op::kNormGather> : Tuned<12, true, 1, 0, 1> {};
-template <> struct Launch<384, Op::kGather> : Tuned<0, false, 0, 3, 4, 3> {};
-template <> struct Launch<384, Op::kAddLn> : Tuned<2, true, 1> {};
-template <> struct Launch<384, Op::kReverseAddLn> : Tuned<2, true, 1> {};
-template <> struct Launch<384, Op::kAddLnAffine> : Tuned<2, true, 1> {};
-template <> struct Launch<384, Op::kLnAffine> : Tuned<4, false> {};
-template <> struct Launch<384, Op::kAddNormGather> : Tuned<4, true> {};
-template <> struct Launch<768, Op::kLn> : Tuned<3, true> {};
-template <> struct Launch<768, Op::kLnAffine> : Tuned<0, false, 1> {};
-template <> struct Launch<768, Op::kGather> : Tuned<0, false, 0, 0, 4, 3> {};
+// Level 2 (C = 384, 32,760 rows): one tile per wave with load priority and the
+// row held in binary32, which leaves the single-input LayerNorm kernels and
+// add_ln so few registers (68-88) that the whole grid is resident at once:
+// each wave issues its loads as it starts and normalises as soon as they land.
+// Against the pipelined loop on a capped grid (binary64 rows): ln_fixed -8%,
+// norm_gather -5%, add_ln -2%, window_reverse_add_ln -1.4%.
+//  * ln_fixed, norm_gather and window_reverse_add_ln: one-wave workgroups;
+//    add_ln and ln_affine: 4-wave workgroups.
+//  * add_norm_gather and add_ln_affine stay on the pipelined loop over a capped
+//    grid with binary64 rows (4 and 2 workgroups per compute unit; one tile per
+//    wave measured 1-5% slower for them).
+//  * plain gather: one-wave workgroups with 2 tiles per wave, all table
+//    entries and rows loaded before the first store (-7.4% against one tile per
+//    wave with 3 resident workgroups per compute unit).
+template <> struct Launch<384, Op::kLn> : Tuned<0, false, 1, 1, float> {};
+template <> struct Launch<384, Op::kNormGather> : Tuned<0, false, 1, 1, float> {};
+template <> struct Launch<384, Op::kGather> : Tuned<0, false, 1, 1, double, 0, 6, 2> {};
+template <> struct Launch<384, Op::kAddLn> : Tuned<0, false, 1, 4, float> {};
+template <> struct Launch<384, Op::kReverseAddLn> : Tuned<0, false, 1, 1, float> {};
+template <> struct Launch<384, Op::kAddLnAffine> : Tuned<2, true, 1, 4, double> {};
+template <> struct Launch<384, Op::kLnAffine> : Tuned<0, false, 1, 4, float> {};
+template <> struct Launch<384, Op::kAddNormGather> : Tuned<4, true, 0, 4, double> {};
+// Patch merge (C = 768, 32,760 rows): ln_fixed one tile per wave in one-wave
+// workgroups, ln_affine in 4-wave workgroups, both with load priority and
+// binary32 rows (-1.3% and -0.8% against the capped pipelined loop).
+template <> struct Launch<768, Op::kLn> : Tuned<0, false, 1, 1, float> {};
+template <> struct Launch<768, Op::kLnAffine> : Tuned<0, false, 1, 4, float> {};
+template <> struct Launch<768, Op::kGather> : Tuned<0, false, 0, 4, double, 3> {};
 
-// The caps above were chosen at the model's sizes, where each wave of a capped
-// grid takes 1.1-2.3 row tiles. On larger inputs a capped grid makes every wave
-// loop over many tiles, and one tile per wave streams better. A capped entry
-// keeps its cap only while its waves would take at most kMaxTilesPerWave tiles
-// each (0 = always). Measured at C = 384 on 65,520 and 131,040 tokens (grids
-// 8 x 182 x 45 and 8 x 364 x 45), cap against one tile per wave: at 131,040 one
-// tile per wave was 1-10% faster for every kernel; at 65,520 it was faster
-// for norm_gather (-4.4%) and add_norm_gather (-6.0%) at 2.9 and 2.2 tiles per
-// wave, and for add_ln, window_reverse_add_ln and add_ln_affine (-3 to -7%) at
-// 4 tiles per wave, but slower for ln_fixed (+2.0%, 2.7 tiles per wave). (The
-// plain gather, then capped, has since gone to one tile per wave at every
-// size.) C = 768 ln_fixed on 131,040 rows: -10.4% with the same limit of 3
-// (its 32,760-row size keeps the cap).
-// The same rule gives C = 192 ln_fixed, add_ln, window_reverse_add_ln and
-// add_ln_affine a cap (4, 3, 3 and 2 workgroups per compute unit) for inputs
-// where their waves take at most 2 tiles: -13% (add_ln), -10%
-// (window_reverse_add_ln, add_ln_affine) at 32,760 rows, -10% and -4%
-// (ln_fixed) at 48,960 and 65,520 rows; at the model's 131,040 rows they run
-// one tile per wave as before. The C = 192 gathers, add_norm_gather and
-// ln_affine gained at most 2% or lost with caps at those sizes.
+// A capped entry keeps its cap only while its waves would take at most
+// kMaxTilesPerWave tiles each (0 = always); on larger inputs a capped grid
+// makes every wave loop over many tiles, and one tile per wave streams better.
+// C = 192 ln_fixed, add_ln, window_reverse_add_ln and add_ln_affine take their
+// caps (4, 3, 3 and 2 workgroups per compute unit) for inputs where their waves
+// take at most 2 tiles: -13% (add_ln), -10% (window_reverse_add_ln,
+// add_ln_affine) at 32,760 rows, -10% and -4% (ln_fixed) at 48,960 and 65,520
+// rows; at the model's 131,040 rows they run one tile per wave.
 template <int C, Op O> constexpr int kMaxTilesPerWave = 0;
-template <> constexpr int kMaxTilesPerWave<384, Op::kLn> = 3;
-template <> constexpr int kMaxTilesPerWave<384, Op::kAddLn> = 3;
-template <> constexpr int kMaxTilesPerWave<384, Op::kReverseAddLn> = 3;
-template <> constexpr int kMaxTilesPerWave<384, Op::kAddLnAffine> = 3;
-template <> constexpr int kMaxTilesPerWave<384, Op::kLnAffine> = 3;
-template <> constexpr int kMaxTilesPerWave<384, Op::kNormGather> = 2;
-template <> constexpr int kMaxTilesPerWave<384, Op::kAddNormGather> = 2;
-template <> constexpr int kMaxTilesPerWave<768, Op::kLn> = 3;
 template <> constexpr int kMaxTilesPerWave<192, Op::kLn> = 2;
 template <> constexpr int kMaxTilesPerWave<192, Op::kAddLn> = 2;
 template <> constexpr int kMaxTilesPerWave<192, Op::kReverseAddLn> = 2;
 template <> constexpr int kMaxTilesPerWave<192, Op::kAddLnAffine> = 2;
-
+template <> constexpr int kMaxTilesPerWave<384, Op::kAddLnAffine> = 3;
+template <> constexpr int kMaxTilesPerWave<384, Op::kAddNormGather> = 2;
 
 // Compute units of the device, queried on first use (0 = not yet known). Only
 // the launch shape of capped grids depends on it, never a result; a failed
@@ -963,25 +1032,25 @@ inline int compute_units() {
 
 template <int C, Op O>
 unsigned grid_for(int64_t rows) {
+    using L = Launch<C, O>;
     static_assert(kChunksOk<C, O>, "a normalising kernel must use its width's chunk count");
-    static_assert(O == Op::kGather || O == Op::kNormGather || Launch<C, O>::kWaves == kBlock / 64,
-                  "only the gathers take their workgroup size from the launch table");
-    static_assert(O == Op::kGather || O == Op::kNormGather || Launch<C, O>::kResident == 0,
-                  "only the gathers reserve LDS to limit their residency");
+    static_assert(O == Op::kGather || L::kTiles == 1, "only the plain gather takes several tiles per wave");
+    static_assert(L::kTiles == 1 || L::kBlocksPerCu == 0, "a multi-tile grid is sized by its tiles, not capped");
     using T = Tile<C, kChunksOf<C, O>>;
-    constexpr int kWaves = Launch<C, O>::kWaves;
     const int64_t tiles = (rows + T::kRowsPerWave - 1) / T::kRowsPerWave;
-    int64_t blocks = (tiles + kWaves - 1) / kWaves;
-    if (Launch<C, O>::kBlocksPerCu > 0) {
-        const int64_t cap = static_cast<int64_t>(compute_units()) * Launch<C, O>::kBlocksPerCu;
+    const int64_t waves = (tiles + L::kTiles - 1) / L::kTiles;
+    int64_t blocks = (waves + L::kWaves - 1) / L::kWaves;
+    if (L::kBlocksPerCu > 0) {
+        const int64_t cap = static_cast<int64_t>(compute_units()) * L::kBlocksPerCu;
         constexpr int kMax = kMaxTilesPerWave<C, O>;
-        if (blocks > cap && (kMax == 0 || tiles <= static_cast<int64_t>(kMax) * cap * kWaves)) blocks = cap;
+        if (blocks > cap && (kMax == 0 || tiles <= static_cast<int64_t>(kMax) * cap * L::kWaves)) blocks = cap;
     }
     // A dispatch counts its work-items in 32 bits: past 2^32 of them (C = 192
     // ln_fixed on more than 2^29 rows) the grid stops at the largest size below
     // that, and the waves loop over the remaining tiles with the grid stride,
-    // as on a capped grid.
-    constexpr int64_t kMaxBlocks = ((int64_t{1} << 32) - 1) / (64 * kWaves);
+    // as on a capped grid. (A multi-tile gather has a table of fewer than 2^31
+    // entries, far below that.)
+    constexpr int64_t kMaxBlocks = ((int64_t{1} << 32) - 1) / (64 * L::kWaves);
     if (blocks > kMaxBlocks) blocks = kMaxBlocks;
     return static_cast<unsigned>(blocks);
 }
@@ -999,32 +1068,107 @@ constexpr size_t lds_reserve() {
     return k == 0 ? 0 : kLdsPerCu / (k + 1) + 1024;
 }
 
+template <int C, Op O>
+dim3 block_of() { return dim3(64 * Launch<C, O>::kWaves); }
+
 template <int C>
 hipError_t ln_fixed_c(const void* x, void* y, int64_t rows, double eps, hipStream_t s) {
-    using L = Launch<C, Op::kLn>;
-    ln_fixed_kernel<C, Width<C>::K, typename L::H, L::kPrefetch><<<grid_for<C, Op::kLn>(rows), kBlock, 0, s>>>(
-        static_cast<const chunk_t*>(x), static_cast<chunk_t*>(y), rows, eps);
+    constexpr Op O = Op::kLn;
+    using L = Launch<C, O>;
+    ln_fixed_kernel<C, Width<C>::K, typename L::H, L::kPrefetch, L::kPriority, L::kWaves, typename L::Row>
+        <<<grid_for<C, O>(rows), block_of<C, O>(), lds_reserve<C, O>(), s>>>(
+            static_cast<const chunk_t*>(x), static_cast<chunk_t*>(y), rows, eps);
     return hipGetLastError();
 }
 
 template <int C>
 hipError_t add_ln_c(const void* b, const void* r, void* ro, void* y, int64_t rows, double eps,
                     hipStream_t s) {
-    using L = Launch<C, Op::kAddLn>;
-    add_ln_kernel<C, Width<C>::K, typename L::H, L::kPrefetch, L::kPriority><<<grid_for<C, Op::kAddLn>(rows), kBlock, 0, s>>>(
-        static_cast<const chunk_t*>(b), static_cast<const chunk_t*>(r), static_cast<chunk_t*>(ro),
-        static_cast<chunk_t*>(y), rows, eps);
+    constexpr Op O = Op::kAddLn;
+    using L = Launch<C, O>;
+    add_ln_kernel<C, Width<C>::K, typename L::H, L::kPrefetch, L::kPriority, L::kWaves, typename L::Row>
+        <<<grid_for<C, O>(rows), block_of<C, O>(), lds_reserve<C, O>(), s>>>(
+            static_cast<const chunk_t*>(b), static_cast<const chunk_t*>(r), static_cast<chunk_t*>(ro),
+            static_cast<chunk_t*>(y), rows, eps);
     return hipGetLastError();
 }
 
-template <int C, bool kNorm>
-hipError_t gather_c(const void* x, int64_t n_src, const int32_t* table, int64_t n_out, double eps,
-                    void* out, hipStream_t s) {
-    constexpr Op O = kNorm ? Op::kNormGather : Op::kGather;
+template <int C>
+hipError_t window_gather_c(const void* x, int64_t n_src, const int32_t* table, int64_t n_out, void* out,
+                           hipStream_t s) {
+    constexpr Op O = Op::kGather;
     using L = Launch<C, O>;
-    gather_kernel<C, kChunksOf<C, O>, kNorm, typename L::H, L::kPrefetch, L::kWaves, L::kPriority>
-        <<<grid_for<C, O>(n_out), 64 * L::kWaves, lds_reserve<C, O>(), s>>>(
-        static_cast<const chunk_t*>(x), n_src, table, n_out, static_cast<chunk_t*>(out), eps);
+    if constexpr (L::kTiles > 1) {
+        gather_tiles_kernel<C, kChunksOf<C, O>, typename L::H, L::kTiles, L::kWaves, L::kPriority>
+            <<<grid_for<C, O>(n_out), block_of<C, O>(), lds_reserve<C, O>(), s>>>(
+                static_cast<const chunk_t*>(x), n_src, table, n_out, static_cast<chunk_t*>(out));
+    } else {
+        gather_kernel<C, kChunksOf<C, O>, false, typename L::H, L::kPrefetch, L::kWaves, L::kPriority,
+                      typename L::Row>
+            <<<grid_for<C, O>(n_out), block_of<C, O>(), lds_reserve<C, O>(), s>>>(
+                static_cast<const chunk_t*>(x), n_src, table, n_out, static_cast<chunk_t*>(out), 0.0);
+    }
+    return hipGetLastError();
+}
+
+template <int C>
+hipError_t norm_gather_c(const void* x, int64_t n_src, const int32_t* table, int64_t n_out, double eps,
+                         void* out, hipStream_t s) {
+    constexpr Op O = Op::kNormGather;
+    using L = Launch<C, O>;
+    gather_kernel<C, Width<C>::K, true, typename L::H, L::kPrefetch, L::kWaves, L::kPriority, typename L::Row>
+        <<<grid_for<C, O>(n_out), block_of<C, O>(), lds_reserve<C, O>(), s>>>(
+            static_cast<const chunk_t*>(x), n_src, table, n_out, static_cast<chunk_t*>(out), eps);
+    return hipGetLastError();
+}
+
+template <int C>
+hipError_t reverse_add_ln_c(const void* win, int64_t n_win, const int32_t* idx, const void* r, void* ro,
+                            void* y, int64_t rows, double eps, hipStream_t s) {
+    constexpr Op O = Op::kReverseAddLn;
+    using L = Launch<C, O>;
+    reverse_add_ln_kernel<C, Width<C>::K, typename L::H, L::kPrefetch, L::kPriority, L::kWaves, typename L::Row>
+        <<<grid_for<C, O>(rows), block_of<C, O>(), lds_reserve<C, O>(), s>>>(
+            static_cast<const chunk_t*>(win), n_win, idx, static_cast<const chunk_t*>(r),
+            static_cast<chunk_t*>(ro), static_cast<chunk_t*>(y), rows, eps);
+    return hipGetLastError();
+}
+
+template <int C>
+hipError_t add_norm_gather_c(const void* b, const void* r, void* ro, int64_t n_src, const int32_t* table,
+                             int64_t n_out, double eps, void* out, hipStream_t s) {
+    constexpr Op O = Op::kAddNormGather;
+    using L = Launch<C, O>;
+    add_norm_gather_kernel<C, Width<C>::K, typename L::H, L::kPrefetch, L::kPriority, L::kWaves, typename L::Row>
+        <<<grid_for<C, O>(n_out), block_of<C, O>(), lds_reserve<C, O>(), s>>>(
+            static_cast<const chunk_t*>(b), static_cast<const chunk_t*>(r), static_cast<chunk_t*>(ro),
+            n_src, table, n_out, static_cast<chunk_t*>(out), eps);
+    return hipGetLastError();
+}
+
+template <int C>
+hipError_t ln_affine_c(const void* x, const void* g, const void* b, void* y, int64_t rows, double eps,
+                       hipStream_t s) {
+    constexpr Op O = Op::kLnAffine;
+    using L = Launch<C, O>;
+    ln_affine_kernel<C, Width<C>::K, typename L::H, L::kPrefetch, L::kPriority, L::kWaves, typename L::Row,
+                     Width<C>::kWideParams>
+        <<<grid_for<C, O>(rows), block_of<C, O>(), lds_reserve<C, O>(), s>>>(
+            static_cast<const chunk_t*>(x), static_cast<const chunk_t*>(g), static_cast<const chunk_t*>(b),
+            static_cast<chunk_t*>(y), rows, eps);
+    return hipGetLastError();
+}
+
+template <int C>
+hipError_t add_ln_affine_c(const void* br, const void* r, const void* g, const void* b, void* ro, void* y,
+                           int64_t rows, double eps, hipStream_t s) {
+    constexpr Op O = Op::kAddLnAffine;
+    using L = Launch<C, O>;
+    add_ln_affine_kernel<C, Width<C>::K, typename L::H, L::kPrefetch, L::kPriority, L::kWaves, typename L::Row,
+                         Width<C>::kWideParams>
+        <<<grid_for<C, O>(rows), block_of<C, O>(), lds_reserve<C, O>(), s>>>(
+            static_cast<const chunk_t*>(br), static_cast<const chunk_t*>(r), static_cast<const chunk_t*>(g),
+            static_cast<const chunk_t*>(b), static_cast<chunk_t*>(ro), static_cast<chunk_t*>(y), rows, eps);
     return hipGetLastError();
 }
 
@@ -1059,12 +1203,12 @@ hipError_t launch_window_index(const WindowGeometry& g, int32_t* table, hipStrea
 
 hipError_t launch_window_gather(const void* x, int64_t n_src, int32_t C, const int32_t* table,
                                 int64_t n_out, void* out, hipStream_t stream) {
-    return by_width(C, [&](auto c) { return gather_c<decltype(c)::value, false>(x, n_src, table, n_out, 0.0, out, stream); });
+    return by_width(C, [&](auto c) { return window_gather_c<decltype(c)::value>(x, n_src, table, n_out, out, stream); });
 }
 
 hipError_t launch_norm_gather(const void* x, int64_t n_src, int32_t C, const int32_t* table,
                               int64_t n_out, double eps, void* out, hipStream_t stream) {
-    return by_width(C, [&](auto c) { return gather_c<decltype(c)::value, true>(x, n_src, table, n_out, eps, out, stream); });
+    return by_width(C, [&](auto c) { return norm_gather_c<decltype(c)::value>(x, n_src, table, n_out, eps, out, stream); });
 }
 
 hipError_t launch_window_inverse(const WindowGeometry& g, int32_t* inverse, hipStream_t stream) {
@@ -1074,32 +1218,10 @@ hipError_t launch_window_inverse(const WindowGeometry& g, int32_t* inverse, hipS
     return hipGetLastError();
 }
 
-template <int C>
-hipError_t reverse_add_ln_c(const void* win, int64_t n_win, const int32_t* idx, const void* r, void* ro,
-                            void* y, int64_t rows, double eps, hipStream_t s) {
-    using L = Launch<C, Op::kReverseAddLn>;
-    reverse_add_ln_kernel<C, Width<C>::K, typename L::H, L::kPrefetch, L::kPriority>
-        <<<grid_for<C, Op::kReverseAddLn>(rows), kBlock, 0, s>>>(
-            static_cast<const chunk_t*>(win), n_win, idx, static_cast<const chunk_t*>(r),
-            static_cast<chunk_t*>(ro), static_cast<chunk_t*>(y), rows, eps);
-    return hipGetLastError();
-}
-
 hipError_t launch_reverse_add_ln(const void* win, int64_t n_win, const int32_t* inverse,
                                  const void* residual, void* residual_out, void* y, int64_t rows,
                                  int32_t C, double eps, hipStream_t stream) {
     return by_width(C, [&](auto c) { return reverse_add_ln_c<decltype(c)::value>(win, n_win, inverse, residual, residual_out, y, rows, eps, stream); });
-}
-
-template <int C>
-hipError_t add_norm_gather_c(const void* b, const void* r, void* ro, int64_t n_src, const int32_t* table,
-                             int64_t n_out, double eps, void* out, hipStream_t s) {
-    using L = Launch<C, Op::kAddNormGather>;
-    add_norm_gather_kernel<C, Width<C>::K, typename L::H, L::kPrefetch>
-        <<<grid_for<C, Op::kAddNormGather>(n_out), kBlock, 0, s>>>(
-            static_cast<const chunk_t*>(b), static_cast<const chunk_t*>(r), static_cast<chunk_t*>(ro),
-            n_src, table, n_out, static_cast<chunk_t*>(out), eps);
-    return hipGetLastError();
 }
 
 hipError_t launch_add_norm_gather(const void* branch, const void* residual, void* residual_out,
@@ -1108,31 +1230,9 @@ hipError_t launch_add_norm_gather(const void* branch, const void* residual, void
     return by_width(C, [&](auto c) { return add_norm_gather_c<decltype(c)::value>(branch, residual, residual_out, n_src, table, n_out, eps, out, stream); });
 }
 
-template <int C>
-hipError_t ln_affine_c(const void* x, const void* g, const void* b, void* y, int64_t rows, double eps,
-                       hipStream_t s) {
-    using L = Launch<C, Op::kLnAffine>;
-    ln_affine_kernel<C, Width<C>::K, typename L::H, L::kPriority, Width<C>::kWideParams>
-        <<<grid_for<C, Op::kLnAffine>(rows), kBlock, 0, s>>>(
-        static_cast<const chunk_t*>(x), static_cast<const chunk_t*>(g), static_cast<const chunk_t*>(b),
-        static_cast<chunk_t*>(y), rows, eps);
-    return hipGetLastError();
-}
-
 hipError_t launch_ln_affine(const void* x, const void* gamma, const void* beta, void* y, int64_t rows,
                             int32_t C, double eps, hipStream_t stream) {
     return by_width(C, [&](auto c) { return ln_affine_c<decltype(c)::value>(x, gamma, beta, y, rows, eps, stream); });
-}
-
-template <int C>
-hipError_t add_ln_affine_c(const void* br, const void* r, const void* g, const void* b, void* ro, void* y,
-                           int64_t rows, double eps, hipStream_t s) {
-    using L = Launch<C, Op::kAddLnAffine>;
-    add_ln_affine_kernel<C, Width<C>::K, typename L::H, L::kPrefetch, L::kPriority, Width<C>::kWideParams>
-        <<<grid_for<C, Op::kAddLnAffine>(rows), kBlock, 0, s>>>(
-            static_cast<const chunk_t*>(br), static_cast<const chunk_t*>(r), static_cast<const chunk_t*>(g),
-            static_cast<const chunk_t*>(b), static_cast<chunk_t*>(ro), static_cast<chunk_t*>(y), rows, eps);
-    return hipGetLastError();
 }
 
 hipError_t launch_add_ln_affine(const void* branch, const void* residual, const void* gamma, const void* beta,
@@ -1149,8 +1249,8 @@ hipError_t launch_bias_gelu(const void* x, const void* bias, void* y, int64_t ro
     const int64_t n4 = rows * cols / 4;
     const unsigned grid = static_cast<unsigned>((n4 + kBlock - 1) / kBlock);
     bias_gelu_kernel<Streaming><<<grid, kBlock, 0, stream>>>(
-        static_cast<const f32x4_t*>(x), static_cast<const f32x4_t*>(bias), static_cast<f32x4_t*>(y), n4,
-        make_fastdiv(static_cast<uint32_t>(cols / 4)));
+        static_cast<const f32x4_t*>(x), static_cast<const f32x4_t*>(bias),
+        static_cast<f32x4_t*>(y), n4, make_fastdiv(static_cast<uint32_t>(cols / 4)));
     return hipGetLastError();
 }
 
