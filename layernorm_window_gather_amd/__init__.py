@@ -99,32 +99,58 @@ def _out_like(out, shape, device, name):
     return out
 
 
-def ln_fixed(x: torch.Tensor, eps: float = EPS, out: torch.Tensor = None) -> torch.Tensor:
-    """LayerNorm over the last dimension (192, 384 or 768) without affine; ``out`` may be ``x``."""
+# Argument checks shared by the plain functions and prepare(): the C ABI takes
+# no buffer lengths, so every size, shape, dtype, layout and device relation it
+# relies on is checked here before any call crosses it (section 6 of "PyTorch +
+# HIP custom fused operator": device, same device, dtype, contiguity, rank,
+# parameter length).
+
+def _check_ln(x, y) -> int:
     rows = _rows(x, "x")
-    y = _out_like(out, x.shape, x.device, "out")
-    lib = _lib.load()
-    with torch.cuda.device(x.device):
-        _lib.check(lib.lwg_ln_fixed(_ptr(x), _ptr(y), rows, x.shape[-1], float(eps), _stream(x.device)))
-    return y
+    _out_like(y, x.shape, x.device, "out")
+    return rows
 
 
-def add_ln(branch: torch.Tensor, residual: torch.Tensor, eps: float = EPS,
-           residual_out: torch.Tensor = None, out: torch.Tensor = None):
-    """Returns (FP16(residual + branch), LayerNorm of it). ``residual_out`` may be
-    ``residual`` or ``branch`` (in-place update); ``out`` may be either input."""
+def _check_add_ln(branch, residual, residual_out, y) -> int:
     rows = _rows(residual, "residual")
     _rows(branch, "branch")
     if tuple(branch.shape) != tuple(residual.shape):
         raise RuntimeError(f"branch shape {tuple(branch.shape)} != residual shape {tuple(residual.shape)}")
     _same_device(residual, ("branch", branch))
-    r = _out_like(residual_out, residual.shape, residual.device, "residual_out")
-    y = _out_like(out, residual.shape, residual.device, "out")
-    lib = _lib.load()
-    with torch.cuda.device(residual.device):
-        _lib.check(lib.lwg_add_ln(_ptr(branch), _ptr(residual), _ptr(r), _ptr(y), rows,
-                                  residual.shape[-1], float(eps), _stream(residual.device)))
-    return r, y
+    _out_like(residual_out, residual.shape, residual.device, "residual_out")
+    _out_like(y, residual.shape, residual.device, "out")
+    return rows
+
+
+def _check_gather(x, table, out, name) -> int:
+    n_src, shape = _gather_args(x, table, name)
+    _out_like(out, shape, x.device, "out")
+    return n_src
+
+
+def _check_reverse_add_ln(rows, inverse, residual, residual_out, y):
+    n_win = _rows(rows, "rows")
+    n = _rows(residual, "residual")
+    if rows.shape[-1] != residual.shape[-1]:
+        raise RuntimeError(f"rows width {rows.shape[-1]} != residual width {residual.shape[-1]}")
+    if not isinstance(inverse, torch.Tensor) or inverse.dtype != torch.int32 or inverse.dim() != 1 \
+            or not inverse.is_contiguous() or inverse.numel() != n:
+        raise RuntimeError("inverse must be a contiguous 1-D int32 tensor with one entry per residual row")
+    _same_device(residual, ("rows", rows), ("inverse", inverse))
+    _out_like(residual_out, residual.shape, residual.device, "residual_out")
+    _out_like(y, residual.shape, residual.device, "out")
+    return n_win, n
+
+
+def _check_add_norm_gather(branch, residual, residual_out, table, out) -> int:
+    n_src, shape = _gather_args(residual, table, "add_norm_gather")
+    _rows(branch, "branch")
+    if tuple(branch.shape) != tuple(residual.shape):
+        raise RuntimeError(f"branch shape {tuple(branch.shape)} != residual shape {tuple(residual.shape)}")
+    _same_device(residual, ("branch", branch))
+    _out_like(residual_out, residual.shape, residual.device, "residual_out")
+    _out_like(out, shape, residual.device, "out")
+    return n_src
 
 
 def _affine_params(gamma, beta, C, device):
@@ -135,12 +161,77 @@ def _affine_params(gamma, beta, C, device):
             raise RuntimeError(f"{name} must be contiguous and on {device}")
 
 
+def _check_ln_affine(x, gamma, beta, y) -> int:
+    rows = _rows(x, "x")
+    _affine_params(gamma, beta, x.shape[-1], x.device)
+    _out_like(y, x.shape, x.device, "out")
+    return rows
+
+
+def _check_add_ln_affine(branch, residual, gamma, beta, residual_out, y) -> int:
+    rows = _check_add_ln(branch, residual, residual_out, y)
+    _affine_params(gamma, beta, residual.shape[-1], residual.device)
+    return rows
+
+
+def _check_bias_gelu(x, bias, out):
+    for name, t in (("x", x), ("bias", bias), ("out", out)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float32:
+            raise RuntimeError(f"{name} must be a float32 tensor")
+        if not t.is_contiguous():
+            raise RuntimeError(f"{name} must be contiguous")
+        if t.device.type != "cuda":
+            raise RuntimeError(f"{name} must be on a GPU device, got {t.device}")
+    if x.dim() < 1 or bias.dim() != 1 or bias.numel() != x.shape[-1]:
+        raise RuntimeError("bias must be 1-D with one entry per column of x")
+    if tuple(out.shape) != tuple(x.shape):
+        raise RuntimeError(f"out has shape {tuple(out.shape)}, expected {tuple(x.shape)}")
+    _same_device(x, ("bias", bias), ("out", out))
+    cols = x.shape[-1]
+    return (x.numel() // cols if cols else 0), cols
+
+
+def _check_table_out(t, n, name):
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.int32 or t.device.type != "cuda" \
+            or not t.is_contiguous() or t.dim() != 1:
+        raise RuntimeError(f"{name} must be a contiguous 1-D int32 GPU tensor")
+    if t.numel() != n:
+        raise RuntimeError(f"{name} has {t.numel()} entries, expected {n}")
+
+
+def ln_fixed(x: torch.Tensor, eps: float = EPS, out: torch.Tensor = None) -> torch.Tensor:
+    """LayerNorm over the last dimension (192, 384 or 768) without affine; ``out`` may be ``x``."""
+    _rows(x, "x")
+    y = torch.empty(x.shape, dtype=torch.float16, device=x.device) if out is None else out
+    rows = _check_ln(x, y)
+    lib = _lib.load()
+    with torch.cuda.device(x.device):
+        _lib.check(lib.lwg_ln_fixed(_ptr(x), _ptr(y), rows, x.shape[-1], float(eps), _stream(x.device)))
+    return y
+
+
+def add_ln(branch: torch.Tensor, residual: torch.Tensor, eps: float = EPS,
+           residual_out: torch.Tensor = None, out: torch.Tensor = None):
+    """Returns (FP16(residual + branch), LayerNorm of it). ``residual_out`` may be
+    ``residual`` or ``branch`` (in-place update); ``out`` may be either input."""
+    _rows(residual, "residual")
+    r = torch.empty(residual.shape, dtype=torch.float16, device=residual.device) if residual_out is None \
+        else residual_out
+    y = torch.empty(residual.shape, dtype=torch.float16, device=residual.device) if out is None else out
+    rows = _check_add_ln(branch, residual, r, y)
+    lib = _lib.load()
+    with torch.cuda.device(residual.device):
+        _lib.check(lib.lwg_add_ln(_ptr(branch), _ptr(residual), _ptr(r), _ptr(y), rows,
+                                  residual.shape[-1], float(eps), _stream(residual.device)))
+    return r, y
+
+
 def ln_affine(x: torch.Tensor, gamma: torch.Tensor, beta: torch.Tensor, eps: float = EPS,
               out: torch.Tensor = None) -> torch.Tensor:
     """LayerNorm over the last dimension with a per-channel scale and shift."""
-    rows = _rows(x, "x")
-    _affine_params(gamma, beta, x.shape[-1], x.device)
-    y = _out_like(out, x.shape, x.device, "out")
+    _rows(x, "x")
+    y = torch.empty(x.shape, dtype=torch.float16, device=x.device) if out is None else out
+    rows = _check_ln_affine(x, gamma, beta, y)
     lib = _lib.load()
     with torch.cuda.device(x.device):
         _lib.check(lib.lwg_ln_affine(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), rows, x.shape[-1], float(eps),
@@ -151,14 +242,11 @@ def ln_affine(x: torch.Tensor, gamma: torch.Tensor, beta: torch.Tensor, eps: flo
 def add_ln_affine(branch: torch.Tensor, residual: torch.Tensor, gamma: torch.Tensor, beta: torch.Tensor,
                   eps: float = EPS, residual_out: torch.Tensor = None, out: torch.Tensor = None):
     """Returns (FP16(residual + branch), affine LayerNorm of it)."""
-    rows = _rows(residual, "residual")
-    _rows(branch, "branch")
-    if tuple(branch.shape) != tuple(residual.shape):
-        raise RuntimeError(f"branch shape {tuple(branch.shape)} != residual shape {tuple(residual.shape)}")
-    _same_device(residual, ("branch", branch))
-    _affine_params(gamma, beta, residual.shape[-1], residual.device)
-    r = _out_like(residual_out, residual.shape, residual.device, "residual_out")
-    y = _out_like(out, residual.shape, residual.device, "out")
+    _rows(residual, "residual")
+    r = torch.empty(residual.shape, dtype=torch.float16, device=residual.device) if residual_out is None \
+        else residual_out
+    y = torch.empty(residual.shape, dtype=torch.float16, device=residual.device) if out is None else out
+    rows = _check_add_ln_affine(branch, residual, gamma, beta, r, y)
     lib = _lib.load()
     with torch.cuda.device(residual.device):
         _lib.check(lib.lwg_add_ln_affine(_ptr(branch), _ptr(residual), _ptr(gamma), _ptr(beta), _ptr(r), _ptr(y),
@@ -168,23 +256,9 @@ def add_ln_affine(branch: torch.Tensor, residual: torch.Tensor, gamma: torch.Ten
 
 def bias_gelu(x: torch.Tensor, bias: torch.Tensor, out: torch.Tensor = None) -> torch.Tensor:
     """float32 gelu(x + bias, tanh form) over the last dimension; ``out`` may be ``x``."""
-    for name, t in (("x", x), ("bias", bias)):
-        if not isinstance(t, torch.Tensor) or t.dtype != torch.float32:
-            raise RuntimeError(f"{name} must be a float32 tensor")
-        if not t.is_contiguous():
-            raise RuntimeError(f"{name} must be contiguous")
-        if t.device.type != "cuda":
-            raise RuntimeError(f"{name} must be on a GPU device, got {t.device}")
-    if x.dim() < 1 or bias.dim() != 1 or bias.numel() != x.shape[-1]:
-        raise RuntimeError("bias must be 1-D with one entry per column of x")
-    _same_device(x, ("bias", bias))
-    cols = x.shape[-1]
-    rows = x.numel() // cols if cols else 0
-    if out is None:
+    if out is None and isinstance(x, torch.Tensor):
         out = torch.empty_like(x)
-    elif out.dtype != torch.float32 or tuple(out.shape) != tuple(x.shape) or not out.is_contiguous() \
-            or out.device != x.device:
-        raise RuntimeError("out must be a contiguous float32 tensor shaped like x")
+    rows, cols = _check_bias_gelu(x, bias, out)
     lib = _lib.load()
     with torch.cuda.device(x.device):
         _lib.check(lib.lwg_bias_gelu(_ptr(x), _ptr(bias), _ptr(out), rows, cols, _stream(x.device)))
@@ -216,8 +290,7 @@ def window_index_build(grid, window, shift=(0, 0, 0), device=None, out: torch.Te
         if dev.type != "cuda":
             raise RuntimeError(f"window tables live on a GPU device, got {dev}")
         out = torch.empty(m, dtype=torch.int32, device=dev)
-    elif out.dtype != torch.int32 or out.device.type != "cuda" or not out.is_contiguous() or out.dim() != 1:
-        raise RuntimeError("out must be a contiguous 1-D int32 GPU tensor")
+    _check_table_out(out, m, "out")
     lib = _lib.load()
     with torch.cuda.device(out.device):
         _lib.check(lib.lwg_window_index_build(*g, *w, *s, ctypes.c_void_p(out.data_ptr()), out.numel(),
@@ -228,28 +301,41 @@ def window_index_build(grid, window, shift=(0, 0, 0), device=None, out: torch.Te
 _tables = {}
 
 
-def _settle(t: torch.Tensor) -> None:
-    """Wait for a newly built cached table, so that any stream may read it later.
-    Inside stream capture the build is part of the graph and no wait is made."""
-    if not torch.cuda.is_current_stream_capturing():
-        torch.cuda.current_stream(t.device).synchronize()
+def _cached_build(cache, key, build, dev):
+    """A table from ``cache``, or built now. A table built outside stream capture
+    is waited for and cached, so that any stream may read it later. One first
+    requested inside stream capture is returned uncached: it is allocated from the
+    graph's memory and only built when the graph replays, so an eager call later
+    builds (and caches) its own."""
+    t = cache.get(key)
+    if t is not None:
+        return t
+    t = build()
+    with torch.cuda.device(dev):
+        if torch.cuda.is_current_stream_capturing():
+            return t
+        torch.cuda.current_stream(dev).synchronize()
+    cache[key] = t
+    return t
+
+
+def _table_device(device) -> torch.device:
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    if dev.type != "cuda":
+        raise RuntimeError(f"window tables live on a GPU device, got {dev}")
+    if dev.index is None:
+        dev = torch.device("cuda", torch.cuda.current_device())
+    return dev
 
 
 def window_table(grid, window, shift=(0, 0, 0), device=None) -> torch.Tensor:
     """Cached ``window_index_build``: one table per (grid, window, shift, device).
     The table is built on the device's current stream at first use, and that
-    first call waits for it, so later calls may use it on any stream."""
+    first call waits for it, so later calls may use it on any stream (a first
+    call inside stream capture returns a table of that graph, uncached)."""
     g, w, s = _triple(grid, "grid"), _triple(window, "window"), _triple(shift, "shift")
-    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
-    if dev.index is None:
-        dev = torch.device("cuda", torch.cuda.current_device())
-    key = (g, w, s, dev.index)
-    t = _tables.get(key)
-    if t is None:
-        t = window_index_build(g, w, s, device=dev)
-        _settle(t)
-        _tables[key] = t
-    return t
+    dev = _table_device(device)
+    return _cached_build(_tables, (g, w, s, dev.index), lambda: window_index_build(g, w, s, device=dev), dev)
 
 
 def _gather_args(x, table, name):
@@ -269,8 +355,9 @@ def _gather_args(x, table, name):
 
 def window_gather(x: torch.Tensor, table: torch.Tensor, out: torch.Tensor = None) -> torch.Tensor:
     """out[j] = x[table[j]] for 0 <= table[j] < N, else a +0.0 row."""
-    n_src, shape = _gather_args(x, table, "window_gather")
-    o = _out_like(out, shape, x.device, "out")
+    _, shape = _gather_args(x, table, "window_gather")
+    o = torch.empty(shape, dtype=torch.float16, device=x.device) if out is None else out
+    n_src = _check_gather(x, table, o, "window_gather")
     lib = _lib.load()
     with torch.cuda.device(x.device):
         _lib.check(lib.lwg_window_gather(_ptr(x), n_src, x.shape[-1], _ptr(table), table.numel(),
@@ -282,8 +369,9 @@ def norm_gather(x: torch.Tensor, table: torch.Tensor, eps: float = EPS,
                 out: torch.Tensor = None) -> torch.Tensor:
     """out[j] = LayerNorm(x[table[j]]) for 0 <= table[j] < N, else a +0.0 row;
     the normalised tensor itself is never written."""
-    n_src, shape = _gather_args(x, table, "norm_gather")
-    o = _out_like(out, shape, x.device, "out")
+    _, shape = _gather_args(x, table, "norm_gather")
+    o = torch.empty(shape, dtype=torch.float16, device=x.device) if out is None else out
+    n_src = _check_gather(x, table, o, "norm_gather")
     lib = _lib.load()
     with torch.cuda.device(x.device):
         _lib.check(lib.lwg_norm_gather(_ptr(x), n_src, x.shape[-1], _ptr(table), table.numel(),
@@ -307,8 +395,7 @@ def window_inverse_build(grid, window, shift=(0, 0, 0), device=None, out: torch.
         if dev.type != "cuda":
             raise RuntimeError(f"window tables live on a GPU device, got {dev}")
         out = torch.empty(n, dtype=torch.int32, device=dev)
-    elif out.dtype != torch.int32 or out.device.type != "cuda" or not out.is_contiguous() or out.dim() != 1:
-        raise RuntimeError("out must be a contiguous 1-D int32 GPU tensor")
+    _check_table_out(out, n, "out")
     lib = _lib.load()
     with torch.cuda.device(out.device):
         _lib.check(lib.lwg_window_inverse_build(*g, *w, *s, ctypes.c_void_p(out.data_ptr()), out.numel(),
@@ -323,16 +410,8 @@ def window_inverse_table(grid, window, shift=(0, 0, 0), device=None) -> torch.Te
     """Cached ``window_inverse_build``: one table per (grid, window, shift, device),
     waited for at first use like ``window_table``."""
     g, w, s = _triple(grid, "grid"), _triple(window, "window"), _triple(shift, "shift")
-    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
-    if dev.index is None:
-        dev = torch.device("cuda", torch.cuda.current_device())
-    key = (g, w, s, dev.index)
-    t = _inverses.get(key)
-    if t is None:
-        t = window_inverse_build(g, w, s, device=dev)
-        _settle(t)
-        _inverses[key] = t
-    return t
+    dev = _table_device(device)
+    return _cached_build(_inverses, (g, w, s, dev.index), lambda: window_inverse_build(g, w, s, device=dev), dev)
 
 
 def window_reverse(rows: torch.Tensor, inverse: torch.Tensor, out: torch.Tensor = None) -> torch.Tensor:
@@ -345,16 +424,11 @@ def window_reverse_add_ln(rows: torch.Tensor, inverse: torch.Tensor, residual: t
                           eps: float = EPS, residual_out: torch.Tensor = None, out: torch.Tensor = None):
     """Returns (FP16(residual + rows[inverse]), LayerNorm of it): the window reverse
     of an attention output fused with the residual add + LayerNorm."""
-    n_win = _rows(rows, "rows")
-    n = _rows(residual, "residual")
-    if rows.shape[-1] != residual.shape[-1]:
-        raise RuntimeError("rows and residual widths differ")
-    if not isinstance(inverse, torch.Tensor) or inverse.dtype != torch.int32 or inverse.dim() != 1 \
-            or not inverse.is_contiguous() or inverse.numel() != n:
-        raise RuntimeError("inverse must be a contiguous 1-D int32 tensor with one entry per residual row")
-    _same_device(residual, ("rows", rows), ("inverse", inverse))
-    r = _out_like(residual_out, residual.shape, residual.device, "residual_out")
-    y = _out_like(out, residual.shape, residual.device, "out")
+    _rows(residual, "residual")
+    r = torch.empty(residual.shape, dtype=torch.float16, device=residual.device) if residual_out is None \
+        else residual_out
+    y = torch.empty(residual.shape, dtype=torch.float16, device=residual.device) if out is None else out
+    n_win, n = _check_reverse_add_ln(rows, inverse, residual, r, y)
     lib = _lib.load()
     with torch.cuda.device(residual.device):
         _lib.check(lib.lwg_window_reverse_add_ln(_ptr(rows), n_win, _ptr(inverse), _ptr(residual), _ptr(r),
@@ -368,13 +442,11 @@ def add_norm_gather(branch: torch.Tensor, residual: torch.Tensor, table: torch.T
     """Returns (FP16(residual + branch), gathered LayerNorm of it): out[j] is the
     LayerNorm of residual_out[table[j]], or zeros for padding. The table's valid
     entries must be distinct and cover every token (window_index_build's are)."""
-    n_src, shape = _gather_args(residual, table, "add_norm_gather")
-    _rows(branch, "branch")
-    if tuple(branch.shape) != tuple(residual.shape):
-        raise RuntimeError(f"branch shape {tuple(branch.shape)} != residual shape {tuple(residual.shape)}")
-    _same_device(residual, ("branch", branch))
-    r = _out_like(residual_out, residual.shape, residual.device, "residual_out")
-    o = _out_like(out, shape, residual.device, "out")
+    _, shape = _gather_args(residual, table, "add_norm_gather")
+    r = torch.empty(residual.shape, dtype=torch.float16, device=residual.device) if residual_out is None \
+        else residual_out
+    o = torch.empty(shape, dtype=torch.float16, device=residual.device) if out is None else out
+    n_src = _check_add_norm_gather(branch, residual, r, table, o)
     lib = _lib.load()
     with torch.cuda.device(residual.device):
         _lib.check(lib.lwg_add_norm_gather(_ptr(branch), _ptr(residual), _ptr(r), n_src, residual.shape[-1],
@@ -408,36 +480,30 @@ def prepare(op: str, *tensors, eps: float = EPS, grid=None, window=None, shift=(
       prepare("window_reverse_add_ln", rows, inverse, residual, residual_out, y)
       prepare("add_norm_gather", branch, residual, residual_out, table, out)
       prepare("ln_affine", x, gamma, beta, y)
-      prepare("add_ln_affine", branch, residual, gamma, beta, residual_out, y)"""
+      prepare("add_ln_affine", branch, residual, gamma, beta, residual_out, y)
+      prepare("bias_gelu", x, bias, y)
+    Every argument error raises RuntimeError here, before anything is enqueued."""
     lib = _lib.load()
     if op == "ln_fixed":
         x, y = tensors
-        rows = _rows(x, "x")
-        _out_like(y, x.shape, x.device, "y")
+        rows = _check_ln(x, y)
         dev = x.device
         fn, args = lib.lwg_ln_fixed, (_ptr(x), _ptr(y), rows, x.shape[-1], float(eps), _stream(dev))
     elif op == "add_ln":
         b, r, ro, y = tensors
-        rows = _rows(r, "residual")
-        _rows(b, "branch")
-        if tuple(b.shape) != tuple(r.shape):
-            raise RuntimeError("branch and residual shapes differ")
-        _out_like(ro, r.shape, r.device, "residual_out")
-        _out_like(y, r.shape, r.device, "y")
+        rows = _check_add_ln(b, r, ro, y)
         dev = r.device
         fn, args = lib.lwg_add_ln, (_ptr(b), _ptr(r), _ptr(ro), _ptr(y), rows, r.shape[-1], float(eps),
                                     _stream(dev))
     elif op == "window_index_build":
         (table,) = tensors
         g, w, s = _triple(grid, "grid"), _triple(window, "window"), _triple(shift, "shift")
-        if table.dtype != torch.int32 or table.device.type != "cuda" or not table.is_contiguous():
-            raise RuntimeError("table must be a contiguous int32 GPU tensor")
+        _check_table_out(table, window_token_count(g, w), "table")
         dev = table.device
         fn, args = lib.lwg_window_index_build, (*g, *w, *s, _ptr(table), table.numel(), _stream(dev))
     elif op in ("window_gather", "norm_gather"):
         x, table, out = tensors
-        n_src, shape = _gather_args(x, table, op)
-        _out_like(out, shape, x.device, "out")
+        n_src = _check_gather(x, table, out, op)
         dev = x.device
         if op == "window_gather":
             fn, args = lib.lwg_window_gather, (_ptr(x), n_src, x.shape[-1], _ptr(table), table.numel(),
@@ -448,54 +514,38 @@ def prepare(op: str, *tensors, eps: float = EPS, grid=None, window=None, shift=(
     elif op == "window_inverse_build":
         (inv,) = tensors
         g, w, s = _triple(grid, "grid"), _triple(window, "window"), _triple(shift, "shift")
-        if inv.dtype != torch.int32 or inv.device.type != "cuda" or not inv.is_contiguous():
-            raise RuntimeError("inverse must be a contiguous int32 GPU tensor")
+        _check_table_out(inv, _token_count(g), "inverse")
         dev = inv.device
         fn, args = lib.lwg_window_inverse_build, (*g, *w, *s, _ptr(inv), inv.numel(), _stream(dev))
     elif op == "window_reverse_add_ln":
         rows, inv, r, ro, y = tensors
-        n_win, n = _rows(rows, "rows"), _rows(r, "residual")
-        _out_like(ro, r.shape, r.device, "residual_out")
-        _out_like(y, r.shape, r.device, "y")
-        if inv.dtype != torch.int32 or inv.numel() != n or not inv.is_contiguous():
-            raise RuntimeError("inverse must be a contiguous int32 tensor with one entry per residual row")
+        n_win, n = _check_reverse_add_ln(rows, inv, r, ro, y)
         dev = r.device
         fn, args = lib.lwg_window_reverse_add_ln, (_ptr(rows), n_win, _ptr(inv), _ptr(r), _ptr(ro), _ptr(y), n,
                                                    r.shape[-1], float(eps), _stream(dev))
     elif op == "add_norm_gather":
         b, r, ro, table, out = tensors
-        n_src, shape = _gather_args(r, table, op)
-        _rows(b, "branch")
-        _out_like(ro, r.shape, r.device, "residual_out")
-        _out_like(out, shape, r.device, "out")
+        n_src = _check_add_norm_gather(b, r, ro, table, out)
         dev = r.device
         fn, args = lib.lwg_add_norm_gather, (_ptr(b), _ptr(r), _ptr(ro), n_src, r.shape[-1], _ptr(table),
                                              table.numel(), float(eps), _ptr(out), _stream(dev))
     elif op == "ln_affine":
         x, g, b, y = tensors
-        rows = _rows(x, "x")
-        _affine_params(g, b, x.shape[-1], x.device)
-        _out_like(y, x.shape, x.device, "y")
+        rows = _check_ln_affine(x, g, b, y)
         dev = x.device
         fn, args = lib.lwg_ln_affine, (_ptr(x), _ptr(g), _ptr(b), _ptr(y), rows, x.shape[-1], float(eps),
                                        _stream(dev))
     elif op == "add_ln_affine":
         br, r, g, b, ro, y = tensors
-        rows = _rows(r, "residual")
-        _rows(br, "branch")
-        _affine_params(g, b, r.shape[-1], r.device)
-        _out_like(ro, r.shape, r.device, "residual_out")
-        _out_like(y, r.shape, r.device, "y")
+        rows = _check_add_ln_affine(br, r, g, b, ro, y)
         dev = r.device
         fn, args = lib.lwg_add_ln_affine, (_ptr(br), _ptr(r), _ptr(g), _ptr(b), _ptr(ro), _ptr(y), rows,
                                            r.shape[-1], float(eps), _stream(dev))
     elif op == "bias_gelu":
         x, b, y = tensors
-        if x.dtype != torch.float32 or b.dtype != torch.float32 or y.dtype != torch.float32:
-            raise RuntimeError("bias_gelu takes float32 tensors")
+        rows, cols = _check_bias_gelu(x, b, y)
         dev = x.device
-        cols = x.shape[-1]
-        fn, args = lib.lwg_bias_gelu, (_ptr(x), _ptr(b), _ptr(y), x.numel() // cols, cols, _stream(dev))
+        fn, args = lib.lwg_bias_gelu, (_ptr(x), _ptr(b), _ptr(y), rows, cols, _stream(dev))
     else:
         raise ValueError(f"unknown op {op!r}")
     return Prepared(fn, args, tensors)

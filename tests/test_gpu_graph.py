@@ -148,3 +148,42 @@ def test_graph_replays_match_eager_calls(dev, C):
             assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), f"replay {rep}: {k} differs from eager"
         if rep == 0:
             check_against_oracle(h, ref, C)
+
+
+def test_table_first_requested_inside_capture_is_not_cached(dev):
+    """A cached window table requested for the first time inside stream capture
+    is allocated from the graph's memory and built only when the graph replays,
+    so it must not enter the cache: an eager request afterwards builds its own.
+    A table cached eagerly beforehand is reused inside capture."""
+    grid, shift = (2, 7, 13), (1, 2, 3)                       # a key no other test uses
+    key = ((2, 7, 13), tuple(WINDOW), shift, dev.index)
+    lwg._tables.pop(key, None)
+    C = 192
+    n, m = int(np.prod(grid)), lwg.window_token_count(grid, WINDOW)
+    x = to_dev(workloads.normal_rows(41, n, C), dev)
+    out = torch.empty(m, C, dtype=torch.float16, device=dev)
+    cached = lwg.window_table(GRID, WINDOW, SHIFT, device=dev)   # cached eagerly, outside capture
+
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):                               # warm-up of the gather itself
+        lwg.norm_gather(x, lwg.window_index_build(grid, WINDOW, shift, device=dev), out=out)
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize(dev)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        t_graph = lwg.window_table(grid, WINDOW, shift, device=dev)
+        assert lwg.window_table(GRID, WINDOW, SHIFT, device=dev) is cached
+        lwg.norm_gather(x, t_graph, out=out)
+    assert key not in lwg._tables
+    ref_table = oracle.window_index_table(grid, WINDOW, shift)
+    for _ in range(3):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize(dev)
+        graph.replay()
+        torch.cuda.synchronize(dev)
+        assert np.array_equal(host(t_graph), ref_table)
+        assert_ln_close(host(out), oracle.norm_gather(host(x), ref_table), "norm_gather on a captured table")
+    eager_table = lwg.window_table(grid, WINDOW, shift, device=dev)
+    assert key in lwg._tables and eager_table.data_ptr() != t_graph.data_ptr()
+    assert np.array_equal(host(eager_table), ref_table)
