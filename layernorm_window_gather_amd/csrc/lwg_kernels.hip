@@ -186,7 +186,7 @@ __device__ __forceinline__ void residual_add(const chunk_t (&branch)[K], chunk_t
 // below 2^-47 after the first and at binary64's own rounding level (measured
 // 2^-52.7) after the second. Inf and NaN give NaN.
 __device__ __forceinline__ double newton_rsqrt(double a, double r) {
-    const double h = 0.5 * a * r;
+    const double h = a * (0.5 * r);    // 0.5 * r is exact; no underflow for subnormal a
     return __builtin_fma(r, __builtin_fma(-h, r, 0.5), r);
 }
 
