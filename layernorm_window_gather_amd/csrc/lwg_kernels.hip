@@ -942,10 +942,11 @@ struct Tuned {
     static constexpr int kChunks = Chunks;
     static constexpr int kTiles = Tiles;
 };
-// Chunks per lane of (width, op): the width's K unless the entry sets kChunks.
-template <int C, Op O> constexpr int kChunksOf = Launch<C, O>::kChunks > 0 ? Launch<C, O>::kChunks : Width<C>::K;
-template <int C, Op O>
-constexpr bool kChunksOk = O == Op::kGather || kChunksOf<C, O> == Width<C>::K;
+// Chunks per lane of a launch entry at width C: the width's K unless the entry
+// sets kChunks.
+template <int C, class L> constexpr int kChunksOf = L::kChunks > 0 ? L::kChunks : Width<C>::K;
+template <int C, Op O, class L>
+constexpr bool kChunksOk = O == Op::kGather || kChunksOf<C, L> == Width<C>::K;
 
 // Level 1 (C = 192, 131,040 rows): every kernel holds its row in binary64.
 //  * ln_fixed, add_ln and the fused residual kernels: the pipelined loop, which
@@ -1011,8 +1012,41 @@ template <> constexpr int kMaxTilesPerWave<192, Op::kAddLnAffine> = 2;
 template <> constexpr int kMaxTilesPerWave<384, Op::kAddLnAffine> = 3;
 template <> constexpr int kMaxTilesPerWave<384, Op::kAddNormGather> = 2;
 
+// Inputs well beyond the model's size. The level-2 entries above keep every
+// wave of a 32,760-token grid resident at once; on inputs several times that,
+// their one-tile-per-wave grids run in many generations, and other forms stream
+// better. LaunchLarge<C, O> is the entry taken once the input has more than
+// kLargeFromTilesPerCu<C, O> row tiles (of the width's K) per compute unit
+// (0 = never). Measured at C = 384 on grids 8 x h x 45 against the entries
+// above (the model's grid is 8 x 91 x 45, 16 tiles per compute unit):
+//  * add_ln and window_reverse_add_ln: 4-wave workgroups, binary64 rows, the
+//    pipelined loop; -6% / -10% at 65,520 tokens, -11% / -9% at 131,040, +7%
+//    / +2% at 48,960 (24 tiles per compute unit), hence from 28 tiles;
+//  * ln_fixed and norm_gather: the same form; -5% / -3% at 131,040, even at
+//    65,520 (32 tiles per compute unit), hence from 48 tiles;
+//  * the plain gather: K = 3 (4 rows per wave), one tile per wave, at most 3
+//    resident 4-wave workgroups per compute unit; -8% at 131,040;
+//  * ln_affine: one-wave workgroups, binary32 rows, load priority, the
+//    pipelined loop; -9% at 131,040.
+template <int C, Op O> struct LaunchLarge : Launch<C, O> {};
+template <int C, Op O> constexpr int kLargeFromTilesPerCu = 0;
+template <> struct LaunchLarge<384, Op::kAddLn> : Tuned<0, true> {};
+template <> struct LaunchLarge<384, Op::kReverseAddLn> : Tuned<0, true> {};
+template <> struct LaunchLarge<384, Op::kLn> : Tuned<0, true> {};
+template <> struct LaunchLarge<384, Op::kNormGather> : Tuned<0, true> {};
+template <> struct LaunchLarge<384, Op::kGather> : Tuned<0, false, 0, 4, double, 3, 3> {};
+template <> struct LaunchLarge<384, Op::kLnAffine> : Tuned<0, true, 1, 1, float> {};
+template <> constexpr int kLargeFromTilesPerCu<384, Op::kAddLn> = 28;
+template <> constexpr int kLargeFromTilesPerCu<384, Op::kReverseAddLn> = 28;
+template <> constexpr int kLargeFromTilesPerCu<384, Op::kLn> = 48;
+template <> constexpr int kLargeFromTilesPerCu<384, Op::kNormGather> = 48;
+template <> constexpr int kLargeFromTilesPerCu<384, Op::kGather> = 48;
+template <> constexpr int kLargeFromTilesPerCu<384, Op::kLnAffine> = 48;
+
 // Compute units of the device, queried on first use (0 = not yet known). Only
-// the launch shape of capped grids depends on it, never a result; a failed
+// launch shapes depend on it (the size of a capped grid, the entry a large
+// input takes), never a result: every entry of an op computes the same row
+// function with the same arithmetic in the same order. A failed
 // query falls back to the MI355X count and clears HIP's last-error state so the
 // launch check that follows does not report it.
 std::atomic<int> g_cus{0};
@@ -1030,13 +1064,12 @@ inline int compute_units() {
     return cus;
 }
 
-template <int C, Op O>
+template <int C, Op O, class L>
 unsigned grid_for(int64_t rows) {
-    using L = Launch<C, O>;
-    static_assert(kChunksOk<C, O>, "a normalising kernel must use its width's chunk count");
+    static_assert(kChunksOk<C, O, L>, "a normalising kernel must use its width's chunk count");
     static_assert(O == Op::kGather || L::kTiles == 1, "only the plain gather takes several tiles per wave");
     static_assert(L::kTiles == 1 || L::kBlocksPerCu == 0, "a multi-tile grid is sized by its tiles, not capped");
-    using T = Tile<C, kChunksOf<C, O>>;
+    using T = Tile<C, kChunksOf<C, L>>;
     const int64_t tiles = (rows + T::kRowsPerWave - 1) / T::kRowsPerWave;
     const int64_t waves = (tiles + L::kTiles - 1) / L::kTiles;
     int64_t blocks = (waves + L::kWaves - 1) / L::kWaves;
@@ -1058,118 +1091,153 @@ unsigned grid_for(int64_t rows) {
 // LDS per compute unit on gfx950 (CDNA4).
 constexpr size_t kLdsPerCu = 160 * 1024;
 
-// Dynamic LDS a workgroup of (C, O) reserves so that at most kResident of them
-// fit on a compute unit (0 when the entry sets no limit). No kernel reads it.
-template <int C, Op O>
+// Dynamic LDS a workgroup of launch entry L reserves so that at most kResident
+// of them fit on a compute unit (0 when the entry sets no limit). No kernel
+// reads it.
+template <class L>
 constexpr size_t lds_reserve() {
-    constexpr int k = Launch<C, O>::kResident;
+    constexpr int k = L::kResident;
     static_assert(k == 0 || kLdsPerCu / (k + 1) + 1024 <= 64 * 1024,
                   "a reservation stays within the 64 KB a workgroup may request at launch");
     return k == 0 ? 0 : kLdsPerCu / (k + 1) + 1024;
 }
 
-template <int C, Op O>
-dim3 block_of() { return dim3(64 * Launch<C, O>::kWaves); }
+template <class L>
+dim3 block_of() { return dim3(64 * L::kWaves); }
+
+template <class L> struct Use { using type = L; };
+
+// Calls f(Use<entry>{}) with the launch entry of (C, O) for an input of `rows`
+// rows (output rows for the gathers).
+template <int C, Op O, class F>
+hipError_t with_launch(int64_t rows, F&& f) {
+    if constexpr (kLargeFromTilesPerCu<C, O> > 0) {
+        constexpr int64_t kRows = Tile<C, Width<C>::K>::kRowsPerWave;
+        const int64_t tiles = (rows + kRows - 1) / kRows;
+        if (tiles > static_cast<int64_t>(kLargeFromTilesPerCu<C, O>) * compute_units())
+            return f(Use<LaunchLarge<C, O>>{});
+    }
+    return f(Use<Launch<C, O>>{});
+}
 
 template <int C>
 hipError_t ln_fixed_c(const void* x, void* y, int64_t rows, double eps, hipStream_t s) {
     constexpr Op O = Op::kLn;
-    using L = Launch<C, O>;
-    ln_fixed_kernel<C, Width<C>::K, typename L::H, L::kPrefetch, L::kPriority, L::kWaves, typename L::Row>
-        <<<grid_for<C, O>(rows), block_of<C, O>(), lds_reserve<C, O>(), s>>>(
-            static_cast<const chunk_t*>(x), static_cast<chunk_t*>(y), rows, eps);
-    return hipGetLastError();
+    return with_launch<C, O>(rows, [&](auto use) {
+        using L = typename decltype(use)::type;
+        ln_fixed_kernel<C, Width<C>::K, typename L::H, L::kPrefetch, L::kPriority, L::kWaves, typename L::Row>
+            <<<grid_for<C, O, L>(rows), block_of<L>(), lds_reserve<L>(), s>>>(
+                static_cast<const chunk_t*>(x), static_cast<chunk_t*>(y), rows, eps);
+        return hipGetLastError();
+    });
 }
 
 template <int C>
 hipError_t add_ln_c(const void* b, const void* r, void* ro, void* y, int64_t rows, double eps,
                     hipStream_t s) {
     constexpr Op O = Op::kAddLn;
-    using L = Launch<C, O>;
-    add_ln_kernel<C, Width<C>::K, typename L::H, L::kPrefetch, L::kPriority, L::kWaves, typename L::Row>
-        <<<grid_for<C, O>(rows), block_of<C, O>(), lds_reserve<C, O>(), s>>>(
-            static_cast<const chunk_t*>(b), static_cast<const chunk_t*>(r), static_cast<chunk_t*>(ro),
-            static_cast<chunk_t*>(y), rows, eps);
-    return hipGetLastError();
+    return with_launch<C, O>(rows, [&](auto use) {
+        using L = typename decltype(use)::type;
+        add_ln_kernel<C, Width<C>::K, typename L::H, L::kPrefetch, L::kPriority, L::kWaves, typename L::Row>
+            <<<grid_for<C, O, L>(rows), block_of<L>(), lds_reserve<L>(), s>>>(
+                static_cast<const chunk_t*>(b), static_cast<const chunk_t*>(r), static_cast<chunk_t*>(ro),
+                static_cast<chunk_t*>(y), rows, eps);
+        return hipGetLastError();
+    });
 }
 
 template <int C>
 hipError_t window_gather_c(const void* x, int64_t n_src, const int32_t* table, int64_t n_out, void* out,
                            hipStream_t s) {
     constexpr Op O = Op::kGather;
-    using L = Launch<C, O>;
-    if constexpr (L::kTiles > 1) {
-        gather_tiles_kernel<C, kChunksOf<C, O>, typename L::H, L::kTiles, L::kWaves, L::kPriority>
-            <<<grid_for<C, O>(n_out), block_of<C, O>(), lds_reserve<C, O>(), s>>>(
-                static_cast<const chunk_t*>(x), n_src, table, n_out, static_cast<chunk_t*>(out));
-    } else {
-        gather_kernel<C, kChunksOf<C, O>, false, typename L::H, L::kPrefetch, L::kWaves, L::kPriority,
-                      typename L::Row>
-            <<<grid_for<C, O>(n_out), block_of<C, O>(), lds_reserve<C, O>(), s>>>(
-                static_cast<const chunk_t*>(x), n_src, table, n_out, static_cast<chunk_t*>(out), 0.0);
-    }
-    return hipGetLastError();
+    return with_launch<C, O>(n_out, [&](auto use) {
+        using L = typename decltype(use)::type;
+        if constexpr (L::kTiles > 1) {
+            gather_tiles_kernel<C, kChunksOf<C, L>, typename L::H, L::kTiles, L::kWaves, L::kPriority>
+                <<<grid_for<C, O, L>(n_out), block_of<L>(), lds_reserve<L>(), s>>>(
+                    static_cast<const chunk_t*>(x), n_src, table, n_out, static_cast<chunk_t*>(out));
+        } else {
+            gather_kernel<C, kChunksOf<C, L>, false, typename L::H, L::kPrefetch, L::kWaves, L::kPriority,
+                          typename L::Row>
+                <<<grid_for<C, O, L>(n_out), block_of<L>(), lds_reserve<L>(), s>>>(
+                    static_cast<const chunk_t*>(x), n_src, table, n_out, static_cast<chunk_t*>(out), 0.0);
+        }
+        return hipGetLastError();
+    });
 }
 
 template <int C>
 hipError_t norm_gather_c(const void* x, int64_t n_src, const int32_t* table, int64_t n_out, double eps,
                          void* out, hipStream_t s) {
     constexpr Op O = Op::kNormGather;
-    using L = Launch<C, O>;
-    gather_kernel<C, Width<C>::K, true, typename L::H, L::kPrefetch, L::kWaves, L::kPriority, typename L::Row>
-        <<<grid_for<C, O>(n_out), block_of<C, O>(), lds_reserve<C, O>(), s>>>(
-            static_cast<const chunk_t*>(x), n_src, table, n_out, static_cast<chunk_t*>(out), eps);
-    return hipGetLastError();
+    return with_launch<C, O>(n_out, [&](auto use) {
+        using L = typename decltype(use)::type;
+        gather_kernel<C, Width<C>::K, true, typename L::H, L::kPrefetch, L::kWaves, L::kPriority,
+                      typename L::Row>
+            <<<grid_for<C, O, L>(n_out), block_of<L>(), lds_reserve<L>(), s>>>(
+                static_cast<const chunk_t*>(x), n_src, table, n_out, static_cast<chunk_t*>(out), eps);
+        return hipGetLastError();
+    });
 }
 
 template <int C>
 hipError_t reverse_add_ln_c(const void* win, int64_t n_win, const int32_t* idx, const void* r, void* ro,
                             void* y, int64_t rows, double eps, hipStream_t s) {
     constexpr Op O = Op::kReverseAddLn;
-    using L = Launch<C, O>;
-    reverse_add_ln_kernel<C, Width<C>::K, typename L::H, L::kPrefetch, L::kPriority, L::kWaves, typename L::Row>
-        <<<grid_for<C, O>(rows), block_of<C, O>(), lds_reserve<C, O>(), s>>>(
-            static_cast<const chunk_t*>(win), n_win, idx, static_cast<const chunk_t*>(r),
-            static_cast<chunk_t*>(ro), static_cast<chunk_t*>(y), rows, eps);
-    return hipGetLastError();
+    return with_launch<C, O>(rows, [&](auto use) {
+        using L = typename decltype(use)::type;
+        reverse_add_ln_kernel<C, Width<C>::K, typename L::H, L::kPrefetch, L::kPriority, L::kWaves,
+                              typename L::Row>
+            <<<grid_for<C, O, L>(rows), block_of<L>(), lds_reserve<L>(), s>>>(
+                static_cast<const chunk_t*>(win), n_win, idx, static_cast<const chunk_t*>(r),
+                static_cast<chunk_t*>(ro), static_cast<chunk_t*>(y), rows, eps);
+        return hipGetLastError();
+    });
 }
 
 template <int C>
 hipError_t add_norm_gather_c(const void* b, const void* r, void* ro, int64_t n_src, const int32_t* table,
                              int64_t n_out, double eps, void* out, hipStream_t s) {
     constexpr Op O = Op::kAddNormGather;
-    using L = Launch<C, O>;
-    add_norm_gather_kernel<C, Width<C>::K, typename L::H, L::kPrefetch, L::kPriority, L::kWaves, typename L::Row>
-        <<<grid_for<C, O>(n_out), block_of<C, O>(), lds_reserve<C, O>(), s>>>(
-            static_cast<const chunk_t*>(b), static_cast<const chunk_t*>(r), static_cast<chunk_t*>(ro),
-            n_src, table, n_out, static_cast<chunk_t*>(out), eps);
-    return hipGetLastError();
+    return with_launch<C, O>(n_out, [&](auto use) {
+        using L = typename decltype(use)::type;
+        add_norm_gather_kernel<C, Width<C>::K, typename L::H, L::kPrefetch, L::kPriority, L::kWaves,
+                               typename L::Row>
+            <<<grid_for<C, O, L>(n_out), block_of<L>(), lds_reserve<L>(), s>>>(
+                static_cast<const chunk_t*>(b), static_cast<const chunk_t*>(r), static_cast<chunk_t*>(ro),
+                n_src, table, n_out, static_cast<chunk_t*>(out), eps);
+        return hipGetLastError();
+    });
 }
 
 template <int C>
 hipError_t ln_affine_c(const void* x, const void* g, const void* b, void* y, int64_t rows, double eps,
                        hipStream_t s) {
     constexpr Op O = Op::kLnAffine;
-    using L = Launch<C, O>;
-    ln_affine_kernel<C, Width<C>::K, typename L::H, L::kPrefetch, L::kPriority, L::kWaves, typename L::Row,
-                     Width<C>::kWideParams>
-        <<<grid_for<C, O>(rows), block_of<C, O>(), lds_reserve<C, O>(), s>>>(
-            static_cast<const chunk_t*>(x), static_cast<const chunk_t*>(g), static_cast<const chunk_t*>(b),
-            static_cast<chunk_t*>(y), rows, eps);
-    return hipGetLastError();
+    return with_launch<C, O>(rows, [&](auto use) {
+        using L = typename decltype(use)::type;
+        ln_affine_kernel<C, Width<C>::K, typename L::H, L::kPrefetch, L::kPriority, L::kWaves, typename L::Row,
+                         Width<C>::kWideParams>
+            <<<grid_for<C, O, L>(rows), block_of<L>(), lds_reserve<L>(), s>>>(
+                static_cast<const chunk_t*>(x), static_cast<const chunk_t*>(g), static_cast<const chunk_t*>(b),
+                static_cast<chunk_t*>(y), rows, eps);
+        return hipGetLastError();
+    });
 }
 
 template <int C>
 hipError_t add_ln_affine_c(const void* br, const void* r, const void* g, const void* b, void* ro, void* y,
                            int64_t rows, double eps, hipStream_t s) {
     constexpr Op O = Op::kAddLnAffine;
-    using L = Launch<C, O>;
-    add_ln_affine_kernel<C, Width<C>::K, typename L::H, L::kPrefetch, L::kPriority, L::kWaves, typename L::Row,
-                         Width<C>::kWideParams>
-        <<<grid_for<C, O>(rows), block_of<C, O>(), lds_reserve<C, O>(), s>>>(
-            static_cast<const chunk_t*>(br), static_cast<const chunk_t*>(r), static_cast<const chunk_t*>(g),
-            static_cast<const chunk_t*>(b), static_cast<chunk_t*>(ro), static_cast<chunk_t*>(y), rows, eps);
-    return hipGetLastError();
+    return with_launch<C, O>(rows, [&](auto use) {
+        using L = typename decltype(use)::type;
+        add_ln_affine_kernel<C, Width<C>::K, typename L::H, L::kPrefetch, L::kPriority, L::kWaves,
+                             typename L::Row, Width<C>::kWideParams>
+            <<<grid_for<C, O, L>(rows), block_of<L>(), lds_reserve<L>(), s>>>(
+                static_cast<const chunk_t*>(br), static_cast<const chunk_t*>(r), static_cast<const chunk_t*>(g),
+                static_cast<const chunk_t*>(b), static_cast<chunk_t*>(ro), static_cast<chunk_t*>(y), rows, eps);
+        return hipGetLastError();
+    });
 }
 
 }  // namespace

@@ -1,16 +1,20 @@
-"""Every row kernel at row counts that exercise both launch shapes of the C = 384
-kernels, with every output element compared against the oracle.
+"""Every row kernel at row counts that exercise each launch shape, with every
+output element compared against the oracle.
 
-* 45,061 rows: each wave of the capped C = 384 grids takes 1.5-2.8 row tiles
-  (ln_fixed: 3 workgroups per compute unit x 4 waves on 256 CUs = 3,072 waves
-  for 5,633 tiles of 8 rows; add_ln: 2,048 waves), within every entry's limit of
-  tiles per wave, and the last tile is part filled (45,061 = 8 x 5,632 + 5).
-* 140,005 rows (C = 384 only): past every entry's limit, so the same kernels
-  run one tile per wave.
-At C = 192 and 768 the grids at 45,061 rows hold one tile per wave (C = 768
-ln_fixed is past its limit there; it runs capped, with waves looping, at the
-32,760-row patch-merge size in tests/test_gpu_widths_affine.py), and the same
-counts end in part-filled tiles.
+* 45,061 rows at C = 384: 5,633 tiles of 8 rows, 22 per compute unit on
+  MI355X's 256: the level-2 entries. ln_fixed, add_ln, window_reverse_add_ln,
+  ln_affine and both gathers run one tile per wave; add_ln_affine and
+  add_norm_gather run capped grids (2 and 4 workgroups per compute unit) whose
+  waves take 1.5-2.8 tiles each. The last tile is part filled
+  (45,061 = 8 x 5,632 + 5).
+* 140,005 rows at C = 384: 68 tiles per compute unit, past every large-input
+  threshold (28 and 48), so ln_fixed, add_ln, window_reverse_add_ln,
+  ln_affine, norm_gather and the plain gather take their large-input entries;
+  add_ln_affine and add_norm_gather are past their tiles-per-wave limits and
+  run one tile per wave. test_large_input_entries_give_the_same_bits checks
+  that both entries give the same bits on the same rows.
+At C = 192 and 768 the grids at 45,061 rows hold one tile per wave, and the
+same counts end in part-filled tiles.
 """
 import numpy as np
 import pytest
@@ -87,3 +91,44 @@ def test_add_norm_gather_with_padding(dev, rows_case):
     r_ref, g_ref = oracle.add_norm_gather(br, res, table)
     assert_bit_exact(host(r), r_ref, f"add_norm_gather residual C={C}")
     assert_ln_close(host(g), g_ref, f"add_norm_gather C={C}")
+
+
+def test_gathers_with_padding(dev, rows_case):
+    # a seeded order of every token, with -1 padding and out-of-range entries mixed in
+    C, _, res, _, _ = rows_case
+    print(f"[passes] window_gather / norm_gather C={C} rows={len(res)}", flush=True)
+    rng = np.random.default_rng(98 + C)
+    table = np.concatenate([np.arange(len(res)), np.full(3001, -1), np.full(7, len(res))])
+    table = table[rng.permutation(table.size)].astype(np.int32)
+    tx, tt = to_dev(res, dev), to_dev(table, dev)
+    assert_bit_exact(host(lwg.window_gather(tx, tt)), oracle.window_gather(res, table), f"window_gather C={C}")
+    assert_ln_close(host(lwg.norm_gather(tx, tt)), oracle.norm_gather(res, table), f"norm_gather C={C}")
+
+
+def test_large_input_entries_give_the_same_bits(dev):
+    """A C = 384 input past the large-input thresholds and its first 40,000 rows
+    (below them) run different launch entries; the shared rows must agree bit
+    for bit, op by op."""
+    C, n, k = 384, 140005, 40000
+    nc, off = workloads.stress_row_classes(190, n)
+    x = to_dev(workloads.mixed_rows(191, n, C, nc, off), dev)
+    b = to_dev(workloads.mixed_rows(192, n, C, nc, off, offset_mean=0.0), dev)
+    g = to_dev(workloads.normal_rows(193, 1, C)[0], dev)
+    bt = to_dev(workloads.normal_rows(194, 1, C, std=0.1)[0], dev)
+    table = to_dev(np.random.default_rng(195).permutation(n).astype(np.int32), dev)
+    inverse = to_dev(np.random.default_rng(196).permutation(n).astype(np.int32), dev)
+    print(f"[passes] large-input entries vs level-2 entries C={C} rows={n}/{k}", flush=True)
+
+    def same(label, full, part):
+        full = full if isinstance(full, tuple) else (full,)
+        part = part if isinstance(part, tuple) else (part,)
+        for f, p in zip(full, part):
+            assert_bit_exact(host(f[:k]), host(p), label)
+
+    same("ln_fixed", lwg.ln_fixed(x), lwg.ln_fixed(x[:k]))
+    same("add_ln", lwg.add_ln(b, x), lwg.add_ln(b[:k], x[:k]))
+    same("ln_affine", lwg.ln_affine(x, g, bt), lwg.ln_affine(x[:k], g, bt))
+    same("window_gather", lwg.window_gather(x, table), lwg.window_gather(x, table[:k]))
+    same("norm_gather", lwg.norm_gather(x, table), lwg.norm_gather(x, table[:k]))
+    same("window_reverse_add_ln", lwg.window_reverse_add_ln(b, inverse, x),
+         lwg.window_reverse_add_ln(b, inverse[:k], x[:k]))
