@@ -992,9 +992,14 @@ template <> struct Launch<384, Op::kAddNormGather> : Tuned<4, true, 0, 4, double
 // Patch merge (C = 768, 32,760 rows): ln_fixed one tile per wave in one-wave
 // workgroups, ln_affine in 4-wave workgroups, both with load priority and
 // binary32 rows (-1.3% and -0.8% against the capped pipelined loop).
+// add_ln and window_reverse_add_ln: the pipelined loop with binary64 rows
+// (-2.8% and -5.2% against the plain loop at 32,760 rows, -4% and -7% at
+// 131,040).
 template <> struct Launch<768, Op::kLn> : Tuned<0, false, 1, 1, float> {};
 template <> struct Launch<768, Op::kLnAffine> : Tuned<0, false, 1, 4, float> {};
 template <> struct Launch<768, Op::kGather> : Tuned<0, false, 0, 4, double, 3> {};
+template <> struct Launch<768, Op::kAddLn> : Tuned<0, true> {};
+template <> struct Launch<768, Op::kReverseAddLn> : Tuned<0, true> {};
 
 // A capped entry keeps its cap only while its waves would take at most
 // kMaxTilesPerWave tiles each (0 = always); on larger inputs a capped grid
@@ -1028,6 +1033,9 @@ template <> constexpr int kMaxTilesPerWave<384, Op::kAddNormGather> = 2;
 //    resident 4-wave workgroups per compute unit; -8% at 131,040;
 //  * ln_affine: one-wave workgroups, binary32 rows, load priority, the
 //    pipelined loop; -9% at 131,040.
+// At C = 768 (4 rows per tile; the patch merge's 32,760 rows are 32 tiles per
+// compute unit) ln_fixed takes the 4-wave, binary64, pipelined form from 40
+// tiles per compute unit: -5% at 48,960 rows and beyond, +4% at 32,760.
 template <int C, Op O> struct LaunchLarge : Launch<C, O> {};
 template <int C, Op O> constexpr int kLargeFromTilesPerCu = 0;
 template <> struct LaunchLarge<384, Op::kAddLn> : Tuned<0, true> {};
@@ -1042,6 +1050,8 @@ template <> constexpr int kLargeFromTilesPerCu<384, Op::kLn> = 48;
 template <> constexpr int kLargeFromTilesPerCu<384, Op::kNormGather> = 48;
 template <> constexpr int kLargeFromTilesPerCu<384, Op::kGather> = 48;
 template <> constexpr int kLargeFromTilesPerCu<384, Op::kLnAffine> = 48;
+template <> struct LaunchLarge<768, Op::kLn> : Tuned<0, true> {};
+template <> constexpr int kLargeFromTilesPerCu<768, Op::kLn> = 40;
 
 // Compute units of the device, queried on first use (0 = not yet known). Only
 // launch shapes depend on it (the size of a capped grid, the entry a large

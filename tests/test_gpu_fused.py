@@ -145,9 +145,11 @@ def test_window_inverse_other_windows(dev, window):
 
 
 def test_in_place_calls_at_level2_size(dev):
-    """In-place use at [32760, 384], where the capped, pipelined grids give each
-    wave more than one row tile (the next tile is read before the current one is
-    written). Every in-place result equals the out-of-place one bit for bit."""
+    """In-place use at [32760, 384]. There add_ln_affine and add_norm_gather run
+    capped, pipelined grids whose waves take more than one row tile (the next
+    tile is read before the current one is written); the other kernels run one
+    tile per wave. Every in-place result equals the out-of-place one bit for
+    bit."""
     lv = workloads.LEVEL2
     n, c = lv.tokens, lv.channels
     x = workloads.normal_rows(81, n, c, mean=0.2, std=1.5)

@@ -218,10 +218,10 @@ def test_gather_out_of_range_entries_are_zero_rows(dev, C):
 
 @pytest.mark.parametrize("C,n_out", [(192, 45061), (384, 45061), (384, 140005), (768, 45061)])
 def test_gathers_loop_over_tiles_with_a_ragged_tail(dev, C, n_out):
-    # 45,061 output rows: 1.8 and 2.75 tiles per wave in the capped C = 384 grids
-    # (12 one-wave workgroups per CU x 8 rows for norm_gather, 4 x 4 waves x 4
-    # rows for the plain gather, on 256 CUs), ending in a part-filled tile.
-    # 140,005 rows: past both entries' limits, one tile per wave.
+    # 45,061 output rows end in a part-filled tile at every width; at C = 384
+    # the plain gather's waves take two tiles each (all loads first).
+    # 140,005 rows at C = 384: past both gathers' large-input thresholds on
+    # 256 CUs, so they run their large-input entries.
     n_src = 20000
     x = workloads.normal_rows(71, n_src, C, mean=0.2, std=1.7)
     table = workloads.table_with_bad_entries(72, n_out, n_src)
@@ -446,7 +446,7 @@ def test_cached_tables_built_on_one_stream_serve_another(dev):
 @pytest.mark.parametrize("shift", [SHIFT, NO_SHIFT])
 def test_level2_norm_gather_and_gather_full(dev, shift):
     """norm_gather and window_gather on the whole level-2 tensor [32760, 384]
-    (capped, pipelined grid: waves take 1.5 tiles), every row compared."""
+    (norm_gather one tile per wave, the plain gather two), every row compared."""
     x, _, scaled = workloads.level2_inputs()
     table = oracle.window_index_table(LEVEL2.grid, WINDOW, shift)
     tt = lwg.window_index_build(LEVEL2.grid, WINDOW, shift, device=dev)

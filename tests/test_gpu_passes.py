@@ -14,7 +14,8 @@ output element compared against the oracle.
   run one tile per wave. test_large_input_entries_give_the_same_bits checks
   that both entries give the same bits on the same rows.
 At C = 192 and 768 the grids at 45,061 rows hold one tile per wave, and the
-same counts end in part-filled tiles.
+same counts end in part-filled tiles; at C = 768 that is 44 tiles of 4 rows per
+compute unit, past ln_fixed's large-input threshold (40).
 """
 import numpy as np
 import pytest
@@ -105,11 +106,11 @@ def test_gathers_with_padding(dev, rows_case):
     assert_ln_close(host(lwg.norm_gather(tx, tt)), oracle.norm_gather(res, table), f"norm_gather C={C}")
 
 
-def test_large_input_entries_give_the_same_bits(dev):
-    """A C = 384 input past the large-input thresholds and its first 40,000 rows
-    (below them) run different launch entries; the shared rows must agree bit
-    for bit, op by op."""
-    C, n, k = 384, 140005, 40000
+@pytest.mark.parametrize("C,n,k", [(384, 140005, 40000), (768, 45061, 20000)])
+def test_large_input_entries_give_the_same_bits(dev, C, n, k):
+    """An input past the large-input thresholds and its first k rows (below
+    them) run different launch entries (at C = 768 only ln_fixed has a second
+    entry); the shared rows must agree bit for bit, op by op."""
     nc, off = workloads.stress_row_classes(190, n)
     x = to_dev(workloads.mixed_rows(191, n, C, nc, off), dev)
     b = to_dev(workloads.mixed_rows(192, n, C, nc, off, offset_mean=0.0), dev)
@@ -117,7 +118,7 @@ def test_large_input_entries_give_the_same_bits(dev):
     bt = to_dev(workloads.normal_rows(194, 1, C, std=0.1)[0], dev)
     table = to_dev(np.random.default_rng(195).permutation(n).astype(np.int32), dev)
     inverse = to_dev(np.random.default_rng(196).permutation(n).astype(np.int32), dev)
-    print(f"[passes] large-input entries vs level-2 entries C={C} rows={n}/{k}", flush=True)
+    print(f"[passes] large-input entries vs the model-size entries C={C} rows={n}/{k}", flush=True)
 
     def same(label, full, part):
         full = full if isinstance(full, tuple) else (full,)

@@ -113,8 +113,8 @@ def test_affine_parameter_checks(dev):
 
 @pytest.mark.parametrize("level,seed", [(workloads.LEVEL1, 31), (workloads.LEVEL2, 32)])
 def test_affine_full_size(dev, level, seed):
-    """Both affine kernels at the workload sizes, where the C = 384 grids are
-    capped and waves take several row tiles."""
+    """Both affine kernels at the workload sizes (at level 2 add_ln_affine runs
+    a capped grid whose waves take two row tiles each)."""
     n, c = level.tokens, level.channels
     nc, off = workloads.stress_row_classes(seed, n)
     res = workloads.mixed_rows(seed + 1, n, c, nc, off)
