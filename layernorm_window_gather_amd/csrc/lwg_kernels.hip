@@ -25,17 +25,19 @@
 //     binary16 values is exact in binary64, so the mean is one rounding of the
 //     exact mean. Where the row's mean is within about 3.9 standard deviations
 //     of zero, the variance is taken in the same pass as the sum (mean of
-//     squares minus squared mean, which is well conditioned there) and each
-//     output is fma(x, rstd, -mean*rstd); other rows (near-constant rows, rows
-//     far from zero mean) take a second pass over the deviations and output
-//     (x - mean) * rstd, as the definition reads. Either way each output is the
-//     correctly rounded binary16 of the exact LayerNorm unless the exact value
-//     lies within about 1e-13 (relative) of a rounding midpoint, where FP32
-//     arithmetic would flip about 1e-4 of outputs by one ulp. The final binary64
-//     -> binary16 rounding goes through a round-to-odd binary32 intermediate,
-//     which makes the two-step conversion exact-once.
+//     squares minus squared mean, which is well conditioned there); other rows
+//     (near-constant rows, rows far from zero mean) take a second pass over the
+//     deviations. Every output is fma(x, rstd, -mean*rstd), with rstd = 0 for a
+//     zero variance (a constant row), whose outputs are then exactly +0. Each
+//     output is the correctly rounded binary16 of the exact LayerNorm unless the
+//     exact value lies within about 2^-43 (relative) of a rounding midpoint, or
+//     on a second-pass row within at most about 2^-38 (absolute); FP32
+//     arithmetic would flip about 1e-4 of outputs by one ulp. The
+//     final binary64 -> binary16 rounding goes through a round-to-odd binary32
+//     intermediate, which makes the two-step conversion exact-once.
 //   * All kernels are stateless and row-local: no atomics, no scratch memory.
-//     Only the affine kernels use LDS, to hold gamma and beta for a workgroup;
+//     Only the affine kernels use LDS, to hold gamma and beta for a workgroup
+//     or a wave;
 //     the plain gathers reserve some, unread, to limit how many of their
 //     workgroups share a compute unit.
 #include <hip/hip_runtime.h>
@@ -455,9 +457,10 @@ __global__ __launch_bounds__(64 * kWaves) void add_ln_kernel(const chunk_t* bran
 }
 
 // Affine LayerNorm and residual add + affine LayerNorm. gamma and beta are
-// binary16 [C]; each workgroup copies them once into LDS and every lane reads
-// its columns from there chunk by chunk, so the parameters neither occupy the
-// vector-memory path nor sit widened in registers. kWide selects the LDS form:
+// binary16 [C]; each workgroup (or each wave, below) copies them into LDS and
+// every lane reads its columns from there chunk by chunk, so the parameters
+// neither occupy the vector-memory path nor sit widened in registers. kWide
+// selects the LDS form:
 // the binary16 chunks (2*C*2 bytes; each use converts 16 values to binary64),
 // or values widened to binary64 as they are staged (2*C*8 bytes, at most
 // 12 KB; each use is a plain LDS read). y may alias x, and residual_out / y may
@@ -488,22 +491,116 @@ __device__ __forceinline__ void stage_params(double* params, const chunk_t* gamm
     __syncthreads();
 }
 
-template <int C, int K, class H, bool kPrefetch, int kPrio, int kWaves, class S, bool kWide>
+// Staging of gamma and beta, by the launch entry's kStage:
+//  * kStageFirst: one copy per workgroup, staged (loaded, written, barrier)
+//    before any row load;
+//  * kWaveCopy: one copy per wave. The wave issues its parameter loads, then
+//    its row loads, then waits for the parameter loads only (issued first, so
+//    the rows stay in flight) and writes its copy. No workgroup barrier: LDS
+//    operations of one wave complete in order, and the fences keep the
+//    compiler from moving the wave's reads of its copy above its writes.
+enum ParamStage : int { kStageFirst = 0, kWaveCopy = 1 };
+
+// The 2*C/8 parameter chunks (gamma, then beta) that the kThreads threads of
+// one copy load, kPerThread per thread.
+template <int C, int kThreads>
+struct ParamChunks {
+    static constexpr int kChunks = C / 8;
+    static constexpr int kPerThread = (2 * kChunks + kThreads - 1) / kThreads;
+    chunk_t v[kPerThread];
+};
+
+template <int C, int kThreads>
+__device__ __forceinline__ ParamChunks<C, kThreads> fetch_params(const chunk_t* gamma, const chunk_t* beta, int t) {
+    using PC = ParamChunks<C, kThreads>;
+    PC p;
+#pragma unroll
+    for (int j = 0; j < PC::kPerThread; ++j) {
+        const int i = t + kThreads * j;
+        p.v[j] = i < PC::kChunks ? gamma[i] : i < 2 * PC::kChunks ? beta[i - PC::kChunks] : chunk_t{0u, 0u, 0u, 0u};
+    }
+    return p;
+}
+
+template <int C, int kThreads>
+__device__ __forceinline__ void put_params(chunk_t* params, const ParamChunks<C, kThreads>& p, int t) {
+    using PC = ParamChunks<C, kThreads>;
+#pragma unroll
+    for (int j = 0; j < PC::kPerThread; ++j) {
+        const int i = t + kThreads * j;
+        if (i < 2 * PC::kChunks) params[i] = p.v[j];
+    }
+}
+
+template <int C, int kThreads>
+__device__ __forceinline__ void put_params(double* params, const ParamChunks<C, kThreads>& p, int t) {
+    using PC = ParamChunks<C, kThreads>;
+#pragma unroll
+    for (int j = 0; j < PC::kPerThread; ++j) {
+        const int i = t + kThreads * j;
+        if (i < 2 * PC::kChunks) {
+            double v[8];
+            unpack8(p.v[j], v);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) params[8 * i + e] = v[e];
+        }
+    }
+}
+
+__device__ __forceinline__ void wave_params_written() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// An affine kernel's parameter staging around its first row loads: begin()
+// before them, end() after; copy() is the copy this thread's wave reads.
+template <int C, int kWaves, bool kWide, int kStage>
+struct AffineParams {
+    using A = AffineStage<C, kWide>;
+    using P = typename A::P;
+    static_assert(kStage == kStageFirst || kStage == kWaveCopy, "unknown parameter staging");
+    static constexpr int kCopies = kStage == kWaveCopy ? kWaves : 1;
+    static constexpr int kThreads = kStage == kWaveCopy ? 64 : 64 * kWaves;
+    static constexpr int kEntries = kCopies * 2 * A::kHalf;
+    P* base;
+    ParamChunks<C, kThreads> fetched;
+    __device__ __forceinline__ int thread() const {
+        return kStage == kWaveCopy ? static_cast<int>(threadIdx.x & 63) : static_cast<int>(threadIdx.x);
+    }
+    __device__ __forceinline__ P* copy() const {
+        return kStage == kWaveCopy ? base + (threadIdx.x >> 6) * 2 * A::kHalf : base;
+    }
+    __device__ __forceinline__ void begin(const chunk_t* gamma, const chunk_t* beta) {
+        if constexpr (kStage == kStageFirst) stage_params<C>(base, gamma, beta);
+        else fetched = fetch_params<C, kThreads>(gamma, beta, thread());
+    }
+    __device__ __forceinline__ void end() {
+        if constexpr (kStage == kWaveCopy) {
+            put_params<C, kThreads>(copy(), fetched, thread());
+            wave_params_written();
+        }
+    }
+};
+
+template <int C, int K, class H, bool kPrefetch, int kPrio, int kWaves, class S, bool kWide, int kStage>
 __global__ __launch_bounds__(64 * kWaves) void ln_affine_kernel(const chunk_t* x, const chunk_t* gamma,
                                                                 const chunk_t* beta, chunk_t* y,
                                                                 int64_t rows, double eps) {
     using T = Tile<C, K>;
-    using A = AffineStage<C, kWide>;
-    __shared__ typename A::P params[2 * A::kHalf];
-    stage_params<C>(params, gamma, beta);
-    const typename A::P* gamma_s = params;
-    const typename A::P* beta_s = params + A::kHalf;
+    using AP = AffineParams<C, kWaves, kWide, kStage>;
+    __shared__ typename AP::P params[AP::kEntries];
+    AP ap{params, {}};
+    ap.begin(gamma, beta);
     const int lane = threadIdx.x & 63;
     const int sub = lane % T::kLanes;
     const int64_t stride = wave_stride_in<kWaves>();
     int64_t w = first_wave_in<kWaves>();
     chunk_t v[K];
     load_tile<C, K, H, kPrio>(x, w, rows, lane, v);
+    ap.end();
+    const typename AP::P* gamma_s = ap.copy();
+    const typename AP::P* beta_s = gamma_s + AP::A::kHalf;
     for (; w * T::kRowsPerWave < rows; w += stride) {
         chunk_t next[K];
         if constexpr (kPrefetch) load_tile<C, K, H, kPrio>(x, w + stride, rows, lane, next);
@@ -521,17 +618,16 @@ __global__ __launch_bounds__(64 * kWaves) void ln_affine_kernel(const chunk_t* x
     }
 }
 
-template <int C, int K, class H, bool kPrefetch, int kPrio, int kWaves, class S, bool kWide>
+template <int C, int K, class H, bool kPrefetch, int kPrio, int kWaves, class S, bool kWide, int kStage>
 __global__ __launch_bounds__(64 * kWaves) void add_ln_affine_kernel(const chunk_t* branch, const chunk_t* residual,
                                                                     const chunk_t* gamma, const chunk_t* beta,
                                                                     chunk_t* residual_out, chunk_t* y,
                                                                     int64_t rows, double eps) {
     using T = Tile<C, K>;
-    using A = AffineStage<C, kWide>;
-    __shared__ typename A::P params[2 * A::kHalf];
-    stage_params<C>(params, gamma, beta);
-    const typename A::P* gamma_s = params;
-    const typename A::P* beta_s = params + A::kHalf;
+    using AP = AffineParams<C, kWaves, kWide, kStage>;
+    __shared__ typename AP::P params[AP::kEntries];
+    AP ap{params, {}};
+    ap.begin(gamma, beta);
     const int lane = threadIdx.x & 63;
     const int sub = lane % T::kLanes;
     const int64_t stride = wave_stride_in<kWaves>();
@@ -539,6 +635,9 @@ __global__ __launch_bounds__(64 * kWaves) void add_ln_affine_kernel(const chunk_
     chunk_t b[K], r[K];
     load_tile<C, K, H, kPrio>(branch, w, rows, lane, b);
     load_tile<C, K, H, kPrio>(residual, w, rows, lane, r);
+    ap.end();
+    const typename AP::P* gamma_s = ap.copy();
+    const typename AP::P* beta_s = gamma_s + AP::A::kHalf;
     for (; w * T::kRowsPerWave < rows; w += stride) {
         chunk_t nb[K], nr[K];
         if constexpr (kPrefetch) {
@@ -917,7 +1016,10 @@ using Streaming = Hints<true, true>;
 //    many workgroups are resident on a compute unit;
 //  * kChunks overrides K (plain gather only: it reduces nothing);
 //  * kTiles > 1 gives each wave that many tiles, all loads first (plain gather
-//    only).
+//    only);
+//  * kStage (affine kernels) is how gamma and beta reach LDS (ParamStage): one
+//    copy per workgroup staged before any row load, or one copy per wave
+//    fetched ahead of the row loads and written after them without a barrier.
 template <int C, Op O> struct Launch {
     using H = Streaming;
     using Row = double;
@@ -928,9 +1030,10 @@ template <int C, Op O> struct Launch {
     static constexpr int kResident = 0;
     static constexpr int kChunks = 0;
     static constexpr int kTiles = 1;
+    static constexpr int kStage = 0;
 };
 template <int Cap, bool Prefetch, int Priority = 0, int Waves = 4, class R = double, int Resident = 0,
-          int Chunks = 0, int Tiles = 1>
+          int Chunks = 0, int Tiles = 1, int Stage = 0>
 struct Tuned {
     using H = Streaming;
     using Row = R;
@@ -941,6 +1044,7 @@ struct Tuned {
     static constexpr int kResident = Resident;
     static constexpr int kChunks = Chunks;
     static constexpr int kTiles = Tiles;
+    static constexpr int kStage = Stage;
 };
 // Chunks per lane of a launch entry at width C: the width's K unless the entry
 // sets kChunks.
@@ -958,6 +1062,8 @@ constexpr bool kChunksOk = O == Op::kGather || kChunksOf<C, L> == Width<C>::K;
 //  * norm_gather: one tile per wave in 4-wave workgroups, at most 6 resident
 //    per compute unit (its 70 registers would allow 7: -1.5%).
 //  * ln_affine: one tile per wave with load priority.
+//  * ln_affine and add_ln_affine: a per-wave copy of gamma and beta (-2.4% and
+//    -1.1% against one copy per workgroup behind a barrier).
 //                                                  Tuned<cap, pipelined, priority, waves, row, resident, chunks, tiles>
 template <> struct Launch<192, Op::kLn> : Tuned<4, true> {};
 template <> struct Launch<192, Op::kGather> : Tuned<0, false, 0, 4, double, 3> {};
@@ -965,8 +1071,8 @@ template <> struct Launch<192, Op::kNormGather> : Tuned<0, false, 0, 4, double, 
 template <> struct Launch<192, Op::kAddLn> : Tuned<3, true> {};
 template <> struct Launch<192, Op::kReverseAddLn> : Tuned<3, true> {};
 template <> struct Launch<192, Op::kAddNormGather> : Tuned<0, true> {};
-template <> struct Launch<192, Op::kAddLnAffine> : Tuned<2, true> {};
-template <> struct Launch<192, Op::kLnAffine> : Tuned<0, false, 1> {};
+template <> struct Launch<192, Op::kAddLnAffine> : Tuned<2, true, 0, 4, double, 0, 0, 1, kWaveCopy> {};
+template <> struct Launch<192, Op::kLnAffine> : Tuned<0, false, 1, 4, double, 0, 0, 1, kWaveCopy> {};
 // Level 2 (C = 384, 32,760 rows): one tile per wave with load priority and the
 // row held in binary32, which leaves the single-input LayerNorm kernels and
 // add_ln so few registers (68-88) that the whole grid is resident at once:
@@ -989,14 +1095,17 @@ template <> struct Launch<384, Op::kReverseAddLn> : Tuned<0, false, 1, 1, float>
 template <> struct Launch<384, Op::kAddLnAffine> : Tuned<2, true, 1, 4, double> {};
 template <> struct Launch<384, Op::kLnAffine> : Tuned<0, false, 1, 4, float> {};
 template <> struct Launch<384, Op::kAddNormGather> : Tuned<4, true, 0, 4, double> {};
-// Patch merge (C = 768, 32,760 rows): ln_fixed one tile per wave in one-wave
-// workgroups, ln_affine in 4-wave workgroups, both with load priority and
-// binary32 rows (-1.3% and -0.8% against the capped pipelined loop).
+// Patch merge (C = 768, 32,760 rows): ln_fixed and ln_affine one tile per wave
+// in one-wave workgroups with load priority and binary32 rows (-1.3% against
+// the capped pipelined loop); ln_affine takes gamma and beta into its wave's
+// own LDS copy behind its first row loads (-3.8% against 4-wave workgroups
+// staging one copy before them). At C = 384 the per-wave copy, widened to
+// binary64, measured +2.4 to +3.5% and is not used.
 // add_ln and window_reverse_add_ln: the pipelined loop with binary64 rows
 // (-2.8% and -5.2% against the plain loop at 32,760 rows, -4% and -7% at
 // 131,040).
 template <> struct Launch<768, Op::kLn> : Tuned<0, false, 1, 1, float> {};
-template <> struct Launch<768, Op::kLnAffine> : Tuned<0, false, 1, 4, float> {};
+template <> struct Launch<768, Op::kLnAffine> : Tuned<0, false, 1, 1, float, 0, 0, 1, kWaveCopy> {};
 template <> struct Launch<768, Op::kGather> : Tuned<0, false, 0, 4, double, 3> {};
 template <> struct Launch<768, Op::kAddLn> : Tuned<0, true> {};
 template <> struct Launch<768, Op::kReverseAddLn> : Tuned<0, true> {};
@@ -1227,7 +1336,7 @@ hipError_t ln_affine_c(const void* x, const void* g, const void* b, void* y, int
     return with_launch<C, O>(rows, [&](auto use) {
         using L = typename decltype(use)::type;
         ln_affine_kernel<C, Width<C>::K, typename L::H, L::kPrefetch, L::kPriority, L::kWaves, typename L::Row,
-                         Width<C>::kWideParams>
+                         Width<C>::kWideParams, L::kStage>
             <<<grid_for<C, O, L>(rows), block_of<L>(), lds_reserve<L>(), s>>>(
                 static_cast<const chunk_t*>(x), static_cast<const chunk_t*>(g), static_cast<const chunk_t*>(b),
                 static_cast<chunk_t*>(y), rows, eps);
@@ -1242,7 +1351,7 @@ hipError_t add_ln_affine_c(const void* br, const void* r, const void* g, const v
     return with_launch<C, O>(rows, [&](auto use) {
         using L = typename decltype(use)::type;
         add_ln_affine_kernel<C, Width<C>::K, typename L::H, L::kPrefetch, L::kPriority, L::kWaves,
-                             typename L::Row, Width<C>::kWideParams>
+                             typename L::Row, Width<C>::kWideParams, L::kStage>
             <<<grid_for<C, O, L>(rows), block_of<L>(), lds_reserve<L>(), s>>>(
                 static_cast<const chunk_t*>(br), static_cast<const chunk_t*>(r), static_cast<const chunk_t*>(g),
                 static_cast<const chunk_t*>(b), static_cast<chunk_t*>(ro), static_cast<chunk_t*>(y), rows, eps);
