@@ -498,8 +498,11 @@ __device__ __forceinline__ void stage_params(double* params, const chunk_t* gamm
 //    its row loads, then waits for the parameter loads only (issued first, so
 //    the rows stay in flight) and writes its copy. No workgroup barrier: LDS
 //    operations of one wave complete in order, and the fences keep the
-//    compiler from moving the wave's reads of its copy above its writes.
-enum ParamStage : int { kStageFirst = 0, kWaveCopy = 1 };
+//    compiler from moving the wave's reads of its copy above its writes;
+//  * kFetchFirst: one copy per workgroup, loaded ahead of the row loads and
+//    written after them, behind a barrier: a slow parameter fetch then
+//    delays only the arithmetic, not the row loads.
+enum ParamStage : int { kStageFirst = 0, kWaveCopy = 1, kFetchFirst = 2 };
 
 // The 2*C/8 parameter chunks (gamma, then beta) that the kThreads threads of
 // one copy load, kPerThread per thread.
@@ -559,7 +562,7 @@ template <int C, int kWaves, bool kWide, int kStage>
 struct AffineParams {
     using A = AffineStage<C, kWide>;
     using P = typename A::P;
-    static_assert(kStage == kStageFirst || kStage == kWaveCopy, "unknown parameter staging");
+    static_assert(kStage == kStageFirst || kStage == kWaveCopy || kStage == kFetchFirst, "unknown parameter staging");
     static constexpr int kCopies = kStage == kWaveCopy ? kWaves : 1;
     static constexpr int kThreads = kStage == kWaveCopy ? 64 : 64 * kWaves;
     static constexpr int kEntries = kCopies * 2 * A::kHalf;
@@ -579,6 +582,9 @@ struct AffineParams {
         if constexpr (kStage == kWaveCopy) {
             put_params<C, kThreads>(copy(), fetched, thread());
             wave_params_written();
+        } else if constexpr (kStage == kFetchFirst) {
+            put_params<C, kThreads>(copy(), fetched, thread());
+            __syncthreads();
         }
     }
 };
@@ -1018,8 +1024,10 @@ using Streaming = Hints<true, true>;
 //  * kTiles > 1 gives each wave that many tiles, all loads first (plain gather
 //    only);
 //  * kStage (affine kernels) is how gamma and beta reach LDS (ParamStage): one
-//    copy per workgroup staged before any row load, or one copy per wave
-//    fetched ahead of the row loads and written after them without a barrier.
+//    copy per workgroup staged before any row load; one copy per wave fetched
+//    ahead of the row loads and written after them without a barrier; or one
+//    copy per workgroup fetched ahead and written after them, behind a
+//    barrier.
 template <int C, Op O> struct Launch {
     using H = Streaming;
     using Row = double;
@@ -1081,6 +1089,11 @@ template <> struct Launch<192, Op::kLnAffine> : Tuned<0, false, 1, 4, double, 0,
 // norm_gather -5%, add_ln -2%, window_reverse_add_ln -1.4%.
 //  * ln_fixed, norm_gather and window_reverse_add_ln: one-wave workgroups;
 //    add_ln and ln_affine: 4-wave workgroups.
+//  * ln_affine loads gamma and beta ahead of its rows and writes them to LDS
+//    after (kFetchFirst). Staged before the row loads, the copy made every
+//    wave wait on a cold parameter fetch first: on some boxes its rounds then
+//    spread 6-13% (9.3-10.7 us); fetched first they stay within 1.5% at
+//    9.6 us, the former mean.
 //  * add_norm_gather and add_ln_affine stay on the pipelined loop over a capped
 //    grid with binary64 rows (4 and 2 workgroups per compute unit; one tile per
 //    wave measured 1-5% slower for them).
@@ -1093,7 +1106,7 @@ template <> struct Launch<384, Op::kGather> : Tuned<0, false, 1, 1, double, 0, 6
 template <> struct Launch<384, Op::kAddLn> : Tuned<0, false, 1, 4, float> {};
 template <> struct Launch<384, Op::kReverseAddLn> : Tuned<0, false, 1, 1, float> {};
 template <> struct Launch<384, Op::kAddLnAffine> : Tuned<2, true, 1, 4, double> {};
-template <> struct Launch<384, Op::kLnAffine> : Tuned<0, false, 1, 4, float> {};
+template <> struct Launch<384, Op::kLnAffine> : Tuned<0, false, 1, 4, float, 0, 0, 1, kFetchFirst> {};
 template <> struct Launch<384, Op::kAddNormGather> : Tuned<4, true, 0, 4, double> {};
 // Patch merge (C = 768, 32,760 rows): ln_fixed and ln_affine one tile per wave
 // in one-wave workgroups with load priority and binary32 rows (-1.3% against
