@@ -3,7 +3,8 @@
 Every C entry point only enqueues kernels on the caller's stream: no
 allocation, no synchronisation, no memset node. So a caller can capture a pass
 of the pipeline once and replay it. The test captures one pass of every
-operation at both widths on a ragged, padded, shifted grid. It replays the
+operation at each served width (192, 384 and 768) on a ragged, padded, shifted
+grid. It replays the
 graph several times, copying new inputs in between with eager work and
 synchronisations around each replay, and checks every replay bit for bit
 against the same calls made eagerly on the same inputs. The eager results of
@@ -104,7 +105,7 @@ def check_against_oracle(h, e, C):
     assert np.all(np.abs(got - ref) <= 2e-5 + 2e-5 * np.abs(ref)), "graph-case bias_gelu"
 
 
-@pytest.mark.parametrize("C", [192, 384])
+@pytest.mark.parametrize("C", [192, 384, 768])
 def test_graph_replays_match_eager_calls(dev, C):
     n = int(np.prod(GRID))
     m = lwg.window_token_count(GRID, WINDOW)
