@@ -300,11 +300,14 @@ SWEEP_ROWS = (16384, 32768, 65536, 131040, 262144, 524288)
 # grids of the C = 384 gather sweep: level 2's 8 x _ x 45 with the grid height varied
 # (32760 tokens at height 91), cut by the (2, 6, 12) window with shift (1, 3, 6)
 GATHER_SWEEP_GRIDS = ((8, 12, 45), (8, 24, 45), (8, 48, 45), (8, 91, 45), (8, 182, 45), (8, 364, 45))
+# the same at C = 192 on grids 8 x h x 90 (level 1 is h = 182)
+GATHER_SWEEP_GRIDS_192 = ((8, 23, 90), (8, 46, 90), (8, 91, 90), (8, 182, 90), (8, 364, 90), (8, 728, 90))
 
 
 def size_sweep(lwg, torch, dev, reps):
     """add_ln and ln_fixed at C = 192 over SWEEP_ROWS, and norm_gather,
-    window_gather and ln_fixed at C = 384 over GATHER_SWEEP_GRIDS, each on a cold
+    window_gather and ln_fixed at C = 384 over GATHER_SWEEP_GRIDS and at C = 192
+    over GATHER_SWEEP_GRIDS_192, each on a cold
     buffer pool, timed like the per-kernel table; a least-squares fit of time =
     fixed + bytes / rate separates the per-launch fixed cost from the streaming
     rate."""
@@ -358,36 +361,40 @@ def size_sweep(lwg, torch, dev, reps):
                   for op, per_row in (("add_ln", 4 * c * HALF), ("ln_fixed", 2 * c * HALF),
                                       ("torch_copy", 2 * c * HALF))}
 
-    # C = 384: the gathers against ln_fixed over the same token counts, in the
-    # level-2 launch configuration; their extra per-launch cost is the fixed term
-    c = 384
-    base = workloads.normal_rows(10, 1 << 15, c)
-    g = {"C": c, "grids": [list(gr) for gr in GATHER_SWEEP_GRIDS], "tokens": [], "rows_out": [],
-         "norm_gather_us": [], "window_gather_us": [], "ln_fixed_us": [], "bytes": {}}
-    nbytes = {"norm_gather": [], "window_gather": [], "ln_fixed": []}
-    for grid in GATHER_SWEEP_GRIDS:
-        n = int(np.prod(grid))
-        m = lwg.window_token_count(grid, WINDOW)
-        g["tokens"].append(n)
-        g["rows_out"].append(m)
-        x0 = torch.from_numpy(np.resize(base, (n, c))).to(dev)
-        table = lwg.window_index_build(grid, WINDOW, SHIFT, device=dev)
-        for op in ("norm_gather", "window_gather", "ln_fixed"):
-            nb = algorithmic_bytes(op, n, m, c)
-            nbytes[op].append(nb)
-            count = max(3, -(-COLD_BYTES // nb) + 1)
-            if op == "ln_fixed":
-                pool = [lwg.prepare(op, xx, torch.empty_like(xx)) for xx in (x0.clone() for _ in range(count))]
-            else:
-                pool = [lwg.prepare(op, x0.clone(), table, torch.empty(m, c, dtype=torch.float16, device=dev))
-                        for _ in range(count)]
-            g[f"{op}_us"].append(round(timed(pool), 3))
-            del pool
-            torch.cuda.empty_cache()
-        del x0, table
-    g["bytes"] = nbytes
-    g["fit"] = {op: fit_of(nbytes[op], g[f"{op}_us"]) for op in nbytes}
-    out["gathers_c384"] = g
+    def gathers(c, grids, seed):
+        """norm_gather, window_gather and ln_fixed at width c over `grids`, in
+        the launch configuration each size takes; their extra per-launch cost
+        is the fixed term of the fit."""
+        base = workloads.normal_rows(seed, 1 << 15, c)
+        g = {"C": c, "grids": [list(gr) for gr in grids], "tokens": [], "rows_out": [],
+             "norm_gather_us": [], "window_gather_us": [], "ln_fixed_us": [], "bytes": {}}
+        nbytes = {"norm_gather": [], "window_gather": [], "ln_fixed": []}
+        for grid in grids:
+            n = int(np.prod(grid))
+            m = lwg.window_token_count(grid, WINDOW)
+            g["tokens"].append(n)
+            g["rows_out"].append(m)
+            x0 = torch.from_numpy(np.resize(base, (n, c))).to(dev)
+            table = lwg.window_index_build(grid, WINDOW, SHIFT, device=dev)
+            for op in ("norm_gather", "window_gather", "ln_fixed"):
+                nb = algorithmic_bytes(op, n, m, c)
+                nbytes[op].append(nb)
+                count = max(3, -(-COLD_BYTES // nb) + 1)
+                if op == "ln_fixed":
+                    pool = [lwg.prepare(op, xx, torch.empty_like(xx)) for xx in (x0.clone() for _ in range(count))]
+                else:
+                    pool = [lwg.prepare(op, x0.clone(), table, torch.empty(m, c, dtype=torch.float16, device=dev))
+                            for _ in range(count)]
+                g[f"{op}_us"].append(round(timed(pool), 3))
+                del pool
+                torch.cuda.empty_cache()
+            del x0, table
+        g["bytes"] = nbytes
+        g["fit"] = {op: fit_of(nbytes[op], g[f"{op}_us"]) for op in nbytes}
+        return g
+
+    out["gathers_c384"] = gathers(384, GATHER_SWEEP_GRIDS, 10)
+    out["gathers_c192"] = gathers(192, GATHER_SWEEP_GRIDS_192, 11)
     return out
 
 
