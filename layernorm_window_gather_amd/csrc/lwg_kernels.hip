@@ -1091,9 +1091,9 @@ template <> struct Launch<192, Op::kLnAffine> : Tuned<0, false, 1, 4, double, 0,
 //    add_ln and ln_affine: 4-wave workgroups.
 //  * ln_affine loads gamma and beta ahead of its rows and writes them to LDS
 //    after (kFetchFirst). Staged before the row loads, the copy made every
-//    wave wait on a cold parameter fetch first: on some boxes its rounds then
-//    spread 6-13% (9.3-10.7 us); fetched first they stay within 1.5% at
-//    9.6 us, the former mean.
+//    wave wait on a cold parameter fetch first: on some MI355X devices its
+//    timings then spread 6-13% (9.3-10.7 us); fetched first they stay within
+//    1.5% at 9.6 us, the former mean.
 //  * add_norm_gather and add_ln_affine stay on the pipelined loop over a capped
 //    grid with binary64 rows (4 and 2 workgroups per compute unit; one tile per
 //    wave measured 1-5% slower for them).
