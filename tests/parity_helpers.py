@@ -1,6 +1,14 @@
 """Comparison helpers shared by the GPU parity tests: bit-exact checks for
 integer, index and bit-copy results, and the LayerNorm tolerance (max-abs 2e-3,
-mean-abs 1e-4 against the oracle, equal NaN positions) for normalised rows."""
+mean-abs 1e-4 against the oracle, equal NaN positions) for normalised rows.
+
+Normalised rows are also held to a mismatch count, 0 by default: the kernels
+round the binary64 LayerNorm once to binary16, so an output can differ from the
+oracle's only when the exact value lies within ~2^-43 (relative) of a rounding
+midpoint, which none of the seeded inputs here comes close to. The kernels are
+deterministic (fixed reduction order, no atomics), so a count above 0 on these
+inputs is a regression in the rounding, reported as a failure rather than as
+a printed number."""
 import numpy as np
 
 MAX_ABS, MEAN_ABS = 2e-3, 1e-4
@@ -28,7 +36,7 @@ def assert_bit_exact(got, ref, label=""):
     assert bad.size == 0, f"{label}: {bad.size} elements differ, first at flat index {bad[:5]}"
 
 
-def assert_ln_close(got, ref, label="", max_mismatch_frac=1e-6):
+def assert_ln_close(got, ref, label="", max_mismatches=0):
     g = np.asarray(got, np.float16).astype(np.float64)
     r = np.asarray(ref, np.float16).astype(np.float64)
     assert g.shape == r.shape, label
@@ -42,7 +50,7 @@ def assert_ln_close(got, ref, label="", max_mismatch_frac=1e-6):
           f"mismatches={mismatches}/{d.size}", flush=True)
     assert d.max() <= MAX_ABS, f"{label}: max-abs {d.max()}"
     assert d.mean() <= MEAN_ABS, f"{label}: mean-abs {d.mean()}"
-    assert mismatches <= max(2, max_mismatch_frac * d.size), f"{label}: {mismatches} mismatches"
+    assert mismatches <= max_mismatches, f"{label}: {mismatches} outputs differ from the oracle"
     return mismatches
 
 
